@@ -1,0 +1,183 @@
+"""Benchmark of the fused-MoE layer on one MI355X.
+
+One step = one moe_forward call over one batch of synthetic inputs resident
+in HBM: route -> prepare -> align -> routed GEMM-1 (+SiLU-mul) -> routed
+GEMM-2 -> shared expert -> finalize.  Default workload: the Mixtral-shaped
+bf16 layer (H=4096, I=14336, E=8, top-2, renormalised softmax, logits
+N(0, 2)) at T=4096 tokens.
+
+Prints ONE JSON line: tokens/s (value), TFLOP/s, per-stage times from HIP
+events recorded on the launch stream, the dominant kernel's roofline
+(routed GEMM-1, MFMA-bound) and the CPU oracle timed on a bounded token
+sample on this host ("cpu_baseline").
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused-MoE layer tokens/s & TFLOP/s (% MFMA peak); finalize GB/s, 1 MI355X"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral@T4096",
+                    help="family@T<tokens>, e.g. mixtral@T4096, deepseek_v3@T8192, llama4@T2048")
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="tokens in the oracle's timed sample")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per launch measured with rocprofv3 counters (json)")
+    return ap.parse_args()
+
+
+def find_spec(name):
+    from workloads import CONFIGS
+    for fam in CONFIGS.values():
+        for s in fam:
+            if s.name == name:
+                return s
+    raise SystemExit(f"unknown workload {name}")
+
+
+def layer_flops(spec):
+    """Algorithmic flops of one layer call: the selected experts only
+    (2 flops per multiply-add), no padding rows."""
+    g = 2 if spec.activation == "silu" else 1
+    routed = 2.0 * spec.T * spec.top_k * spec.H * spec.I * (g + 1)
+    shared = 2.0 * spec.T * spec.H * spec.shared_I * (g + 1)
+    return routed, shared
+
+
+def gemm1_flops(spec):
+    g = 2 if spec.activation == "silu" else 1
+    return 2.0 * spec.T * spec.top_k * spec.H * spec.I * g
+
+
+def cpu_baseline(spec, d, sample_n):
+    import numpy as np
+    import oracle
+    from workloads import to_numpy_bits
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    keys = ("w13", "w13_scale", "w2", "w2_scale", "shared_w13", "shared_w13_scale", "shared_w2",
+            "shared_w2_scale")
+    hw = {k: to_numpy_bits(d[k]) for k in keys if d.get(k) is not None}
+    x = to_numpy_bits(d["x"])
+    logits = d["logits"].cpu().numpy()
+    res = to_numpy_bits(d.get("residual"))
+    gam = to_numpy_bits(d.get("gamma"))
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(spec.T, size=min(sample_n, spec.T), replace=False))
+    t0 = time.perf_counter()
+    oracle.forward(x, logits, hw, spec.top_k, spec.scoring, spec.renormalize, 16,
+                   spec.apply_router_weight_on_input, spec.quant, spec.activation, "mirrored",
+                   res, gam, spec.eps, spec.out_quant, tokens=sample)
+    dt = time.perf_counter() - t0
+    return {"value": round(sample.size / dt, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{sample.size} of {spec.T} tokens (route+align over all {spec.T}), "
+                      f"numpy float64, mirrored mode, {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note, not implemented)"}))
+        sys.exit(2)
+    import torch
+    import mixture_experts_layer_routing_amd as moe
+    from workloads import make_layer_inputs
+
+    spec = find_spec(a.workload)
+    dev = "cuda"
+    d = make_layer_inputs(spec, device=dev)
+    w = moe.make_weights(*(d.get(k) for k in ("w13", "w2", "w13_scale", "w2_scale", "shared_w13",
+                                              "shared_w2", "shared_w13_scale", "shared_w2_scale")))
+    bm = a.block_m or moe.moe_pick_block_m(spec.T, spec.top_k, spec.E)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None, ws=None, out=None):
+        return moe.moe_forward(d["x"], d["logits"], w, spec.top_k, spec.scoring, spec.renormalize,
+                               spec.apply_router_weight_on_input, spec.activation, bm,
+                               d.get("residual"), d.get("gamma"), spec.eps, spec.out_quant,
+                               output=out, workspace=ws, stage_events=events)
+
+    out, _, ws = step()
+    for _ in range(a.warmup):
+        step(ws=ws, out=out)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.NUM_STAGE_EVENTS)]
+           for _ in range(a.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(events=evs[i], ws=ws, out=out)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / a.steps
+    stage = {}
+    for j in range(1, moe.NUM_STAGE_EVENTS):
+        vals = [evs[i][j - 1].elapsed_time(evs[i][j]) for i in range(a.steps)]
+        stage[moe.STAGES[j]] = sum(vals) / len(vals)
+    routed, shared = layer_flops(spec)
+    tflops = (routed + shared) / (ms * 1e-3) / 1e12
+    dtype = "fp8" if spec.quant == "fp8" else "bf16"
+    g1_ms = stage["gemm1"]
+    g1_tflops = gemm1_flops(spec) / (g1_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(a.traffic):
+        try:
+            tr = json.load(open(a.traffic))
+            traffic = tr.get(spec.name, {}).get("gemm1_bytes")
+        except Exception:
+            traffic = None
+    line = {
+        "metric": METRIC,
+        "value": round(spec.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; random-init weights of the stated shapes)",
+        "config": {"workload": spec.name, "T": spec.T, "H": spec.H, "I": spec.I, "E": spec.E,
+                   "top_k": spec.top_k, "scoring": spec.scoring, "renormalize": spec.renormalize,
+                   "quant": spec.quant, "shared_I": spec.shared_I, "block_m": bm,
+                   "parallelism": "none (1 GPU)"},
+        "tflops": round(tflops, 2),
+        "mfma_peak_frac": round(tflops / PEAK_TFLOPS[dtype], 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage.items()},
+        "wall_s": round(wall, 3),
+        "roofline": {"kernel": "routed GEMM-1 (gate+up, SiLU-mul fused)", "bound": "mfma",
+                     "achieved": round(g1_tflops, 2), "peak": PEAK_TFLOPS[dtype],
+                     "unit": "TFLOP/s", "frac": round(g1_tflops / PEAK_TFLOPS[dtype], 4),
+                     "traffic": traffic},
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(spec, d, a.cpu_sample)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,249 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused-MoE layer library, libmoe.so.
+ *
+ * The library computes one Mixture-of-Experts layer on one GPU with no data
+ * or expert parallelism, as the modular "prepare -> experts -> finalize"
+ * path with the no-op (no dispatch/combine) prepare/finalize of the pages:
+ *
+ *   "Fused MoE Kernel Features" (vLLM design doc): modular kernels split
+ *     into a prepare/finalize object and an experts object; prepare takes
+ *     "standard"-format activations and emits the quantised type, finalize
+ *     returns standard format in the original dtype; quant formats G(128)
+ *     (per-token group of 128), A (per token), T (per tensor); for top_k == 1
+ *     some models apply the router weight to the input instead of the output.
+ *   "[vLLM] MoE Oracle & Prepare/Finalize": the no-DP/EP prepare(a1,
+ *     topk_weights, topk_ids, ..., apply_router_weight_on_input,
+ *     quant_config) and finalize(output, fused_expert_output, topk_weights,
+ *     topk_ids, ...) contracts.
+ *   "[flashinfer] MoE Finalize + AllReduce fusion": finalize fused with the
+ *     optional shared-expert row, residual add and RMSNorm (hidden 7168).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer unless marked (host).  The
+ *     caller allocates and owns all memory; the library never allocates,
+ *     frees or keeps a pointer after returning.
+ *   - bf16 tensors are passed as uint16_t bit patterns, fp8 tensors as
+ *     uint8_t OCP E4M3 codes (bias 7, no infinities, max finite 448);
+ *     all tensors are dense row-major with the shapes given.
+ *   - Work is enqueued asynchronously on `stream`; nothing synchronises the
+ *     host.  Argument errors are detected on the host BEFORE anything is
+ *     enqueued (no partial work) and returned as a moe_status; device-side
+ *     faults surface at the caller's next synchronisation.  A launch failure
+ *     reported by the HIP runtime is returned as MOE_ERR_HIP.
+ *   - T == 0 is a valid no-op wherever T appears (moe_align still writes its
+ *     zero counts/offsets).
+ *   - moe_last_error() returns a thread-local message for the last failing
+ *     call on the calling thread.
+ *   - The library holds no state besides its compiled kernels; calls on
+ *     different streams with disjoint outputs may overlap.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null required pointer, bad size, top_k out of range, ... */
+  MOE_ERR_UNSUPPORTED = 2,  /* a valid request outside what the kernels implement */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_bytes query */
+  MOE_ERR_HIP = 4           /* the HIP runtime reported a launch error */
+} moe_status;
+
+typedef enum moe_scoring {
+  MOE_SCORING_SOFTMAX = 0,  /* softmax over all E logits */
+  MOE_SCORING_SIGMOID = 1   /* elementwise sigmoid */
+} moe_scoring;
+
+typedef enum moe_quant {
+  MOE_QUANT_NONE = 0,       /* bf16 activations and weights */
+  MOE_QUANT_FP8_G128 = 1    /* fp8 E4M3: activations with one fp32 scale per (row, 128-column
+                               group), the pages' "G(128)"; weights with one fp32 scale per
+                               128x128 block of each matrix */
+} moe_quant;
+
+typedef enum moe_activation {
+  MOE_ACT_SILU_MUL = 0,     /* z = silu(gate) * up, silu(v) = v / (1 + exp(-v)) ("silu") */
+  MOE_ACT_SILU_NO_MUL = 1   /* z = silu(W1 a), no up projection ("silu_no_mul") */
+} moe_activation;
+
+/* Number of events moe_forward records when given a stage_events array. */
+#define MOE_NUM_STAGE_EVENTS 8
+
+/*
+ * Expert weights (host struct holding device pointers).
+ *   R = 2*inter for MOE_ACT_SILU_MUL (rows [0, I) = gate W1, rows [I, 2I) = up W3),
+ *       inter   for MOE_ACT_SILU_NO_MUL (W1 only).
+ *   w13        [E, R, H]   bf16 bits, or E4M3 codes (quant == MOE_QUANT_FP8_G128)
+ *   w13_scale  [E, R/128, H/128] fp32 block scales (fp8 only, else NULL)
+ *   w2         [E, H, I]
+ *   w2_scale   [E, H/128, I/128]
+ *   shared_*   the always-on shared expert, same layouts without the E axis and
+ *              with I_s = shared_inter; shared_inter == 0 means no shared expert.
+ */
+typedef struct moe_weights {
+  int32_t num_experts;
+  int32_t inter;
+  int32_t quant;
+  int32_t shared_inter;
+  const void* w13;
+  const float* w13_scale;
+  const void* w2;
+  const float* w2_scale;
+  const void* shared_w13;
+  const float* shared_w13_scale;
+  const void* shared_w2;
+  const float* shared_w2_scale;
+} moe_weights;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(int status);
+
+/* Thread-local description of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * moe_route -- top-k routing over router logits.
+ * The pages consume topk_ids/topk_weights without defining them; the rule
+ * implemented: per token, experts by descending logit, ties to the lower
+ * expert index, first top_k kept (slot j = j-th largest).  Weights:
+ *   SOFTMAX, renormalize=1: w_j = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0)
+ *   SOFTMAX, renormalize=0: w_j = exp(l_j - max) / sum_{e<E} exp(l_e - max)
+ *   SIGMOID, renormalize=1: w_j = sig(l_j) / sum_{j'<k} sig(l_j')
+ *   SIGMOID, renormalize=0: w_j = sig(l_j)
+ *   logits       [T, E] fp32, finite (precondition)
+ *   topk_ids     [T, top_k] int32 out;  topk_weights [T, top_k] fp32 out
+ * Limits: 1 <= E <= 1024, 1 <= top_k <= min(E, 64); else MOE_ERR_INVALID_ARG.
+ */
+int moe_route(const float* logits, int T, int E, int top_k, int scoring, int renormalize,
+              int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/*
+ * moe_prepare -- the no-DP/EP prepare ("[vLLM] MoE Oracle & Prepare/Finalize"):
+ * if apply_router_weight_on_input, top_k must be 1 (else MOE_ERR_INVALID_ARG,
+ * the page's assert) and a = bf16(a1 * bf16(topk_weights)); then quantise:
+ *   MOE_QUANT_NONE:     a1q [T, H] bf16 = a        (a1q_scale unused, may be NULL)
+ *   MOE_QUANT_FP8_G128: per (t, g): s = max(amax, 1e-10) / 448 (fp32),
+ *                       q = E4M3_rne_sat(a / s);   a1q [T, H] E4M3, a1q_scale [T, H/128] fp32
+ *   a1             [T, H] bf16
+ *   topk_weights   [T, top_k] fp32 (read only when apply_router_weight_on_input)
+ * Limits: H % 8 == 0; H % 128 == 0 for fp8.  a1q may alias a1 only for
+ * MOE_QUANT_NONE.
+ */
+int moe_prepare(const uint16_t* a1, int T, int H, const float* topk_weights, int top_k,
+                int apply_router_weight_on_input, int quant, void* a1q, float* a1q_scale,
+                hipStream_t stream);
+
+/*
+ * moe_align -- sort the T*top_k flat rows i = t*top_k + j by expert into
+ * block_m-padded groups (deterministic; only one result is correct):
+ *   expert_counts[e]   = #{i : ids[i] == e}                                  [E]
+ *   expert_offsets[0]  = 0, [e+1] = [e] + ceil(counts[e] / block_m) * block_m  [E+1]
+ *   sorted_token_ids   = per expert, its flat rows in ascending order, then
+ *                        the pad sentinel T*top_k up to the next offset; the
+ *                        sentinel also fills [offsets[E], sorted capacity)     [sorted cap]
+ *   block_expert_ids[b]= expert owning slots [b*block_m, (b+1)*block_m), -1
+ *                        for blocks at or past offsets[E]                     [block cap]
+ *   num_tokens_post_padded[0] = offsets[E]                                    [1]
+ * Capacities (moe_align_capacity): sorted cap = T*k + min(E, T*k)*(block_m-1),
+ * block cap = ceil(sorted cap / block_m).  workspace: moe_align_workspace_bytes.
+ * Limits: block_m in {16, 32, 64, 128, 256}; 1 <= E <= 1024; ids in [0, E)
+ * (precondition; out-of-range ids are dropped from every output).
+ */
+int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
+              int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token_ids,
+              int32_t* block_expert_ids, int32_t* num_tokens_post_padded,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* (host) capacities of sorted_token_ids and block_expert_ids. */
+int moe_align_capacity(int T, int top_k, int E, int block_m,
+                       int64_t* sorted_capacity, int64_t* block_capacity);
+/* (host) workspace moe_align needs (may be 0). */
+size_t moe_align_workspace_bytes(int T, int top_k, int E, int block_m);
+
+/*
+ * moe_experts -- the modular experts stage ("Fused MoE Kernel Features":
+ * modular experts take pre-quantised input and return the original dtype):
+ * for every flat row i = t*k + j with e = topk_ids[t, j]
+ *   h = W13[e] a[t] (fp32 accumulation), z = act(h),
+ *   fused_expert_output[t, j, :] = bf16(W2[e] z)                  [T, top_k, H] bf16 out
+ * z is held in bf16 (MOE_QUANT_NONE) or re-quantised to E4M3 G(128) along I
+ * (fp8) between the two grouped GEMMs.  With a shared expert, additionally
+ *   shared_out[t, :] = bf16(W2s act(W13s s[t]))                    [T, H] bf16 out
+ * where s = shared_in/shared_in_scale, the unweighted input in a1q's format
+ * (pass a1q when the router weight was not applied on the input).
+ *   a1q, a1q_scale      prepare's output ([T, H] + [T, H/128] fp32 for fp8)
+ *   sorted_token_ids, block_expert_ids, num_tokens_post_padded: moe_align's
+ *                       output for the same topk_ids and block_m
+ *   workspace           moe_experts_workspace_bytes bytes
+ * Limits: H % 64 == 0 and I % 64 == 0 (bf16), H % 128 == 0 and I % 128 == 0 (fp8);
+ * weights->quant must equal the activation format.
+ */
+int moe_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
+                const float* shared_in_scale, int T, int H, int top_k,
+                const moe_weights* weights /* host */, int activation,
+                const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
+                const int32_t* num_tokens_post_padded, int block_m,
+                uint16_t* fused_expert_output, uint16_t* shared_out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* (host) workspace moe_experts needs. */
+size_t moe_experts_workspace_bytes(int T, int H, int top_k, const moe_weights* weights,
+                                   int activation, int block_m);
+
+/*
+ * moe_finalize -- the no-DP/EP finalize (weight-and-reduce over the top-k
+ * expert rows) with the flashinfer finalize fusions:
+ *   acc[t] = sum_j w'[t,j] * y[t,j,:]   (slot order; w' = 1 when the weight was
+ *            applied on the input -- applied to the input instead of the output)
+ *          + shared[t] + residual[t]    (each optional, NULL = absent)
+ *   out[t] = acc[t] / sqrt(mean(acc[t]^2) + eps) * gamma    if gamma != NULL
+ *          = acc[t]                                         otherwise
+ *   output [T, H]: bf16 (out_quant NONE) or E4M3 + output_scale [T, H/128] fp32
+ *   residual_out [T, H] bf16 = bf16(acc) when non-NULL
+ *   fused_expert_output [T, top_k, H] bf16; topk_weights [T, top_k] fp32;
+ *   topk_ids [T, top_k] is accepted for the pages' signature and not read
+ *   (no expert map without EP); gamma [H] bf16.
+ * Limits: H % 8 == 0, H <= 16384; H % 128 == 0 for fp8 output; 1 <= top_k <= 64.
+ */
+int moe_finalize(void* output, float* output_scale, int out_quant,
+                 const uint16_t* fused_expert_output, const float* topk_weights,
+                 const int32_t* topk_ids, int T, int top_k, int H,
+                 int apply_router_weight_on_input, const uint16_t* shared,
+                 const uint16_t* residual, uint16_t* residual_out, const uint16_t* gamma,
+                 float eps, hipStream_t stream);
+
+/*
+ * moe_forward -- the whole layer, enqueued on one stream with no host sync:
+ * route -> prepare -> align -> experts (routed GEMM-1, GEMM-2, shared expert)
+ * -> finalize, intermediates in `workspace`.
+ *   x [T, H] bf16; logits [T, E] fp32; weights (host struct) as moe_experts;
+ *   block_m 0 = choose (moe_pick_block_m); residual/gamma/residual_out as
+ *   moe_finalize; output/output_scale per out_quant.
+ *   stage_events (host array, may be NULL): MOE_NUM_STAGE_EVENTS caller-created
+ *   hipEvents recorded on `stream` at: start, after route, prepare, align,
+ *   routed GEMM-1, routed GEMM-2, shared expert, finalize.
+ */
+int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
+                int scoring, int renormalize, int apply_router_weight_on_input,
+                const moe_weights* weights /* host */, int activation, int block_m,
+                const uint16_t* residual, const uint16_t* gamma, float eps, int out_quant,
+                void* output, float* output_scale, uint16_t* residual_out,
+                void* workspace, size_t workspace_bytes,
+                hipEvent_t* stage_events /* host, nullable */, hipStream_t stream);
+/* (host) workspace moe_forward needs for these sizes (block_m 0 = chosen). */
+size_t moe_forward_workspace_bytes(int T, int H, int top_k, const moe_weights* weights,
+                                   int activation, int block_m,
+                                   int apply_router_weight_on_input);
+/* (host) the block_m moe_forward uses when given 0. */
+int moe_pick_block_m(int T, int top_k, int num_experts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,156 @@
+// finalize: the weight-and-reduce over each token's top-k expert rows
+// ("[vLLM] MoE Oracle & Prepare/Finalize", no-DP/EP finalize) fused with the
+// shared-expert row, residual add, RMSNorm and an optional fp8 G(128) output
+// (the single-GPU part of the flashinfer finalize program, "[flashinfer] MoE
+// Finalize + AllReduce fusion ...", introduction).
+//
+// HBM-bound: one 256-thread workgroup per token; thread tid owns the 16-byte
+// chunks c = tid + 256*i of the row (8 bf16 each), so every load and store is
+// a coalesced 16-byte access and each operand is read exactly once.  The
+// accumulated row stays in registers between the sum-of-squares reduction
+// (wave butterfly, then 4 partials in LDS) and the normalised store.  With an
+// fp8 output, 16 consecutive lanes own one 128-column group.
+#include "moe_device.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
+  const u32x4 r = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(r[i]);
+    f[2 * i + 1] = bf16_to_f32(r[i] >> 16);
+  }
+}
+
+__device__ __forceinline__ void store8_bf16(uint16_t* p, const float* f) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  *reinterpret_cast<u32x4*>(p) = o;
+}
+
+template <int MAXC, bool FP8OUT>
+__global__ __launch_bounds__(256) void finalize_kernel(
+    void* __restrict__ output, float* __restrict__ out_scale,
+    const uint16_t* __restrict__ y, const float* __restrict__ w, int top_k, int H,
+    int weight_on_input, const uint16_t* __restrict__ shared, const uint16_t* __restrict__ residual,
+    uint16_t* __restrict__ residual_out, const uint16_t* __restrict__ gamma, float eps) {
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nch = H / 8;
+  const size_t row = static_cast<size_t>(t) * H;
+  float acc[MAXC][8];
+  float sumsq = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = tid + 256 * i;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[i][v] = 0.f;
+    if (c < nch) {
+      for (int j = 0; j < top_k; ++j) {
+        const float wj = weight_on_input ? 1.0f : w[static_cast<size_t>(t) * top_k + j];
+        float f[8];
+        load8(y + (static_cast<size_t>(t) * top_k + j) * H + c * 8, f);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[i][v] += wj * f[v];
+      }
+      if (shared) {
+        float f[8];
+        load8(shared + row + c * 8, f);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[i][v] += f[v];
+      }
+      if (residual) {
+        float f[8];
+        load8(residual + row + c * 8, f);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[i][v] += f[v];
+      }
+      if (residual_out) store8_bf16(residual_out + row + c * 8, acc[i]);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) sumsq += acc[i][v] * acc[i][v];
+    }
+  }
+  float r = 1.0f;
+  if (gamma) {
+    __shared__ float part[4];
+    const float ws = wave_sum(sumsq);
+    if ((tid & 63) == 0) part[tid >> 6] = ws;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+  }
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = tid + 256 * i;
+    float o[8];
+    if (c < nch) {
+      float g[8];
+      if (gamma) {
+        load8(gamma + c * 8, g);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) o[v] = acc[i][v] * r * g[v];
+      } else {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) o[v] = acc[i][v];
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) o[v] = 0.f;
+    }
+    if constexpr (FP8OUT) {
+      // nch is a multiple of 16 (H % 128 == 0): 16-lane groups are uniform.
+      if (256 * i < nch) {
+        float amax = 0.f;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) amax = fmaxf(amax, __builtin_fabsf(o[v]));
+        amax = group_max<16>(amax);
+        const float s = fmaxf(amax, kQuantEps) / kFp8Max;
+        if (c < nch) {
+          u32x2 q;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) word |= f32_to_e4m3(o[4 * h + v] / s) << (8 * v);
+            q[h] = word;
+          }
+          *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(output) + row + c * 8) = q;
+          if ((tid & 15) == 0) out_scale[static_cast<size_t>(t) * (H / 128) + (c >> 4)] = s;
+        }
+      }
+    } else {
+      if (c < nch) store8_bf16(static_cast<uint16_t*>(output) + row + c * 8, o);
+    }
+  }
+}
+
+template <int MAXC>
+void launch_fin(void* out, float* out_scale, int out_quant, const uint16_t* y, const float* w,
+                int T, int k, int H, int woi, const uint16_t* sh, const uint16_t* res,
+                uint16_t* res_out, const uint16_t* gamma, float eps, hipStream_t s) {
+  if (out_quant == 1)
+    finalize_kernel<MAXC, true><<<T, 256, 0, s>>>(out, out_scale, y, w, k, H, woi, sh, res,
+                                                  res_out, gamma, eps);
+  else
+    finalize_kernel<MAXC, false><<<T, 256, 0, s>>>(out, out_scale, y, w, k, H, woi, sh, res,
+                                                   res_out, gamma, eps);
+}
+
+}  // namespace
+
+void launch_finalize(void* out, float* out_scale, int out_quant, const uint16_t* y,
+                     const float* w, int T, int k, int H, int woi, const uint16_t* sh,
+                     const uint16_t* res, uint16_t* res_out, const uint16_t* gamma, float eps,
+                     hipStream_t s) {
+  const int nch = H / 8;
+  if (nch <= 256) launch_fin<1>(out, out_scale, out_quant, y, w, T, k, H, woi, sh, res, res_out, gamma, eps, s);
+  else if (nch <= 512) launch_fin<2>(out, out_scale, out_quant, y, w, T, k, H, woi, sh, res, res_out, gamma, eps, s);
+  else if (nch <= 1024) launch_fin<4>(out, out_scale, out_quant, y, w, T, k, H, woi, sh, res, res_out, gamma, eps, s);
+  else launch_fin<8>(out, out_scale, out_quant, y, w, T, k, H, woi, sh, res, res_out, gamma, eps, s);
+}
+
+}  // namespace moe

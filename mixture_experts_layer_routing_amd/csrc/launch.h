@@ -1,0 +1,63 @@
+// Internal launchers (host side) of the HIP kernels.  Arguments are checked
+// by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace moe {
+
+void launch_route(const float* logits, int T, int E, int top_k, int scoring, int renorm,
+                  int32_t* ids, float* w, hipStream_t s);
+
+void launch_prepare(const uint16_t* a1, int T, int H, const float* w, int apply_weight,
+                    int quant, void* a1q, float* a1q_scale, hipStream_t s);
+
+size_t align_workspace_bytes(int64_t n, int E);
+void launch_align(const int32_t* ids, int64_t n, int E, int BM, int32_t* counts,
+                  int32_t* offsets, int32_t* sorted, int64_t sorted_cap, int32_t* block_ids,
+                  int64_t block_cap, int32_t* ntp, void* ws, hipStream_t s);
+
+void launch_finalize(void* out, float* out_scale, int out_quant, const uint16_t* y,
+                     const float* w, int T, int k, int H, int woi, const uint16_t* sh,
+                     const uint16_t* res, uint16_t* res_out, const uint16_t* gamma, float eps,
+                     hipStream_t s);
+
+// One grouped-GEMM launch (see gemm_impl.h).
+struct GemmParams {
+  const uint8_t* a;        // activation rows: bf16 or fp8 bytes, row length K
+  const float* a_scale;    // fp8: [rows][K/128]
+  const uint8_t* w;        // expert 0's (or the shared expert's) weight matrix [n_w][K]
+  const float* w_scale;    // fp8: [n_w/128][K/128] per expert
+  int64_t w_stride;        // bytes between consecutive experts' matrices
+  int64_t ws_stride;       // floats between consecutive experts' scale grids
+  int K;                   // reduction length in elements
+  int inter;               // gated: row offset of the up half (I)
+  int n_tiles;             // output column tiles
+  const int32_t* sorted;   // align outputs (routed launches)
+  const int32_t* block_expert;
+  const int32_t* ntp;
+  int T, top_k;
+  void* out;               // z / fused_expert_output / shared_out
+  float* out_scale;        // fp8 z scales [rows][ldo/128]
+  int ldo;                 // output row length in elements
+};
+
+enum GemmKind {
+  GEMM_Z_ROUTED = 0,   // first GEMM of the routed experts (gather), activation, z out
+  GEMM_Y_ROUTED = 1,   // second GEMM of the routed experts, scatter to [T, k, H]
+  GEMM_Z_DENSE = 2,    // first GEMM of the shared expert over all T rows
+  GEMM_Y_DENSE = 3     // second GEMM of the shared expert
+};
+
+// Output column tile of a launch (BNZ: z columns for the first GEMM, H
+// columns for the second).
+int gemm_tile_n(int kind, bool fp8, bool gated, int block_m);
+// Launch one grouped GEMM; max_mblk bounds the M-blocks (grid sizing).
+void launch_gemm_bf16(int kind, bool gated, int block_m, const GemmParams& p, int64_t max_mblk,
+                      hipStream_t s);
+void launch_gemm_fp8(int kind, bool gated, int block_m, const GemmParams& p, int64_t max_mblk,
+                     hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,526 @@
+// C ABI of libmoe.so: argument checks, workspace sizing and kernel launches.
+// The declarations and the contract of every entry point are in moe.h.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Bump allocator over the caller's workspace (sizes only when base is null).
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+struct Caps {
+  int64_t sorted_cap, block_cap;
+};
+
+Caps capacities(int T, int top_k, int E, int bm) {
+  const int64_t n = static_cast<int64_t>(T) * top_k;
+  const int64_t cap = n + std::min<int64_t>(E, n) * (bm - 1);
+  return {cap, (cap + bm - 1) / bm};
+}
+
+int dense_block_m(int T) {
+  if (T <= 16) return 16;
+  if (T <= 32) return 32;
+  if (T <= 64) return 64;
+  return 128;
+}
+
+int check_weights(const moe_weights* w, int H, int activation, bool need_ptrs) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (w->num_experts < 1 || w->num_experts > 1024)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts %d outside [1, 1024]", w->num_experts);
+  if (w->quant != MOE_QUANT_NONE && w->quant != MOE_QUANT_FP8_G128)
+    return fail(MOE_ERR_UNSUPPORTED, "weight quant %d not supported", w->quant);
+  if (activation != MOE_ACT_SILU_MUL && activation != MOE_ACT_SILU_NO_MUL)
+    return fail(MOE_ERR_UNSUPPORTED, "activation %d not supported", activation);
+  if (H <= 0 || H % 128) return fail(MOE_ERR_UNSUPPORTED, "H=%d must be a positive multiple of 128", H);
+  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const bool gated = activation == MOE_ACT_SILU_MUL;
+  const int step = (!fp8 && gated) ? 64 : 128;
+  if (w->inter <= 0 || w->inter % step)
+    return fail(MOE_ERR_UNSUPPORTED, "I=%d must be a positive multiple of %d", w->inter, step);
+  if (w->shared_inter < 0 || (w->shared_inter > 0 && w->shared_inter % step))
+    return fail(MOE_ERR_UNSUPPORTED, "shared I=%d must be a multiple of %d", w->shared_inter, step);
+  if (need_ptrs) {
+    if (!w->w13 || !w->w2) return fail(MOE_ERR_INVALID_ARG, "w13/w2 is NULL");
+    if (fp8 && (!w->w13_scale || !w->w2_scale))
+      return fail(MOE_ERR_INVALID_ARG, "fp8 weights need w13_scale and w2_scale");
+    if (w->shared_inter > 0) {
+      if (!w->shared_w13 || !w->shared_w2) return fail(MOE_ERR_INVALID_ARG, "shared weights are NULL");
+      if (fp8 && (!w->shared_w13_scale || !w->shared_w2_scale))
+        return fail(MOE_ERR_INVALID_ARG, "fp8 shared weights need scales");
+    }
+  }
+  return MOE_OK;
+}
+
+// Workspace of the experts stage: z for the routed rows and for the shared
+// expert, in the GEMM input format of the second GEMM.
+size_t experts_ws(int T, int top_k, const moe_weights* w, int bm, Carve& c, void** z,
+                  float** zs, void** zsh, float** zshs) {
+  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const size_t eb = fp8 ? 1 : 2;
+  const Caps cp = capacities(T, top_k, w->num_experts, bm);
+  const int64_t rows = cp.block_cap * bm;
+  const size_t start = c.used;
+  *z = c.take(static_cast<size_t>(rows) * w->inter * eb);
+  *zs = fp8 ? static_cast<float*>(c.take(static_cast<size_t>(rows) * (w->inter / 128) * 4)) : nullptr;
+  *zsh = nullptr;
+  *zshs = nullptr;
+  if (w->shared_inter > 0) {
+    *zsh = c.take(static_cast<size_t>(T) * w->shared_inter * eb);
+    if (fp8) *zshs = static_cast<float*>(c.take(static_cast<size_t>(T) * (w->shared_inter / 128) * 4));
+  }
+  return c.used - start;
+}
+
+struct StageEvents {
+  hipEvent_t* ev;
+  hipStream_t s;
+  void mark(int i) const {
+    if (ev) (void)hipEventRecord(ev[i], s);
+  }
+};
+
+int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
+                const float* shared_in_scale, int T, int H, int top_k, const moe_weights* w,
+                int activation, const int32_t* sorted, const int32_t* block_expert,
+                const int32_t* ntp, int bm, uint16_t* feo, uint16_t* shared_out, void* ws,
+                const StageEvents& se, hipStream_t s) {
+  using namespace moe;
+  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const bool gated = activation == MOE_ACT_SILU_MUL;
+  const size_t eb = fp8 ? 1 : 2;
+  const int E = w->num_experts, I = w->inter;
+  const int R = gated ? 2 * I : I;
+  Carve c(ws);
+  void *z, *zsh;
+  float *zs, *zshs;
+  experts_ws(T, top_k, w, bm, c, &z, &zs, &zsh, &zshs);
+  const Caps cp = capacities(T, top_k, E, bm);
+  auto launch = [&](int kind, int blk_m, const GemmParams& p, int64_t max_mblk) {
+    if (fp8) launch_gemm_fp8(kind, gated, blk_m, p, max_mblk, s);
+    else launch_gemm_bf16(kind, gated, blk_m, p, max_mblk, s);
+  };
+  // routed first GEMM: gather a1q rows, activation, z [rows, I]
+  GemmParams p{};
+  p.a = static_cast<const uint8_t*>(a1q);
+  p.a_scale = a1q_scale;
+  p.w = static_cast<const uint8_t*>(w->w13);
+  p.w_scale = w->w13_scale;
+  p.w_stride = static_cast<int64_t>(R) * H * eb;
+  p.ws_stride = static_cast<int64_t>(R / 128) * (H / 128);
+  p.K = H;
+  p.inter = I;
+  p.n_tiles = I / gemm_tile_n(GEMM_Z_ROUTED, fp8, gated, bm);
+  p.sorted = sorted;
+  p.block_expert = block_expert;
+  p.ntp = ntp;
+  p.T = T;
+  p.top_k = top_k;
+  p.out = z;
+  p.out_scale = zs;
+  p.ldo = I;
+  launch(GEMM_Z_ROUTED, bm, p, cp.block_cap);
+  se.mark(4);
+  // routed second GEMM: z rows -> fused_expert_output[sorted row]
+  GemmParams q{};
+  q.a = static_cast<const uint8_t*>(z);
+  q.a_scale = zs;
+  q.w = static_cast<const uint8_t*>(w->w2);
+  q.w_scale = w->w2_scale;
+  q.w_stride = static_cast<int64_t>(H) * I * eb;
+  q.ws_stride = static_cast<int64_t>(H / 128) * (I / 128);
+  q.K = I;
+  q.inter = 0;
+  q.n_tiles = H / gemm_tile_n(GEMM_Y_ROUTED, fp8, gated, bm);
+  q.sorted = sorted;
+  q.block_expert = block_expert;
+  q.ntp = ntp;
+  q.T = T;
+  q.top_k = top_k;
+  q.out = feo;
+  q.ldo = H;
+  launch(GEMM_Y_ROUTED, bm, q, cp.block_cap);
+  se.mark(5);
+  if (w->shared_inter > 0) {
+    const int Is = w->shared_inter;
+    const int Rs = gated ? 2 * Is : Is;
+    const int dbm = dense_block_m(T);
+    const int64_t mblk = (T + dbm - 1) / dbm;
+    GemmParams d{};
+    d.a = static_cast<const uint8_t*>(shared_in);
+    d.a_scale = shared_in_scale;
+    d.w = static_cast<const uint8_t*>(w->shared_w13);
+    d.w_scale = w->shared_w13_scale;
+    d.K = H;
+    d.inter = Is;
+    d.n_tiles = Is / gemm_tile_n(GEMM_Z_DENSE, fp8, gated, dbm);
+    d.T = T;
+    d.top_k = 1;
+    d.out = zsh;
+    d.out_scale = zshs;
+    d.ldo = Is;
+    (void)Rs;
+    launch(GEMM_Z_DENSE, dbm, d, mblk);
+    GemmParams e{};
+    e.a = static_cast<const uint8_t*>(zsh);
+    e.a_scale = zshs;
+    e.w = static_cast<const uint8_t*>(w->shared_w2);
+    e.w_scale = w->shared_w2_scale;
+    e.K = Is;
+    e.n_tiles = H / gemm_tile_n(GEMM_Y_DENSE, fp8, gated, dbm);
+    e.T = T;
+    e.top_k = 1;
+    e.out = shared_out;
+    e.ldo = H;
+    launch(GEMM_Y_DENSE, dbm, e, mblk);
+  }
+  se.mark(6);
+  return check_launch("moe_experts");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_pick_block_m(int T, int top_k, int num_experts) {
+  if (T <= 0 || top_k <= 0 || num_experts <= 0) return 16;
+  const int64_t avg = (static_cast<int64_t>(T) * top_k + num_experts - 1) / num_experts;
+  if (avg <= 16) return 16;
+  if (avg <= 32) return 32;
+  if (avg <= 96) return 64;
+  return 128;
+}
+
+int moe_route(const float* logits, int T, int E, int top_k, int scoring, int renormalize,
+              int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", E);
+  if (top_k < 1 || top_k > std::min(E, 64))
+    return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1, min(E, 64)]", top_k);
+  if (scoring != MOE_SCORING_SOFTMAX && scoring != MOE_SCORING_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "scoring=%d", scoring);
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  moe::launch_route(logits, T, E, top_k, scoring, renormalize ? 1 : 0, topk_ids, topk_weights,
+                    stream);
+  return check_launch("moe_route");
+}
+
+int moe_prepare(const uint16_t* a1, int T, int H, const float* topk_weights, int top_k,
+                int apply_router_weight_on_input, int quant, void* a1q, float* a1q_scale,
+                hipStream_t stream) {
+  g_err[0] = 0;
+  if (T < 0 || H <= 0 || H % 8) return fail(MOE_ERR_INVALID_ARG, "T=%d H=%d", T, H);
+  if (quant != MOE_QUANT_NONE && quant != MOE_QUANT_FP8_G128)
+    return fail(MOE_ERR_UNSUPPORTED, "quant %d not supported", quant);
+  if (quant == MOE_QUANT_FP8_G128 && H % 128)
+    return fail(MOE_ERR_INVALID_ARG, "fp8 G(128) needs H %% 128 == 0 (H=%d)", H);
+  if (apply_router_weight_on_input && top_k != 1)
+    return fail(MOE_ERR_INVALID_ARG, "router weight on the input needs top_k == 1 (got %d)", top_k);
+  if (T == 0) return MOE_OK;
+  if (!a1 || !a1q || (apply_router_weight_on_input && !topk_weights) ||
+      (quant == MOE_QUANT_FP8_G128 && !a1q_scale))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (quant == MOE_QUANT_FP8_G128 && static_cast<const void*>(a1) == a1q)
+    return fail(MOE_ERR_INVALID_ARG, "a1q may not alias a1 for fp8");
+  moe::launch_prepare(a1, T, H, topk_weights, apply_router_weight_on_input ? 1 : 0, quant, a1q,
+                      a1q_scale, stream);
+  return check_launch("moe_prepare");
+}
+
+int moe_align_capacity(int T, int top_k, int E, int block_m, int64_t* sorted_capacity,
+                       int64_t* block_capacity) {
+  g_err[0] = 0;
+  if (T < 0 || top_k < 1 || E < 1 || !valid_block_m(block_m))
+    return fail(MOE_ERR_INVALID_ARG, "T=%d top_k=%d E=%d block_m=%d", T, top_k, E, block_m);
+  const Caps c = capacities(T, top_k, E, block_m);
+  if (sorted_capacity) *sorted_capacity = c.sorted_cap;
+  if (block_capacity) *block_capacity = c.block_cap;
+  return MOE_OK;
+}
+
+size_t moe_align_workspace_bytes(int T, int top_k, int E, int block_m) {
+  (void)block_m;
+  if (T <= 0 || top_k <= 0 || E <= 0) return 0;
+  return moe::align_workspace_bytes(static_cast<int64_t>(T) * top_k, E);
+}
+
+int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
+              int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token_ids,
+              int32_t* block_expert_ids, int32_t* num_tokens_post_padded, void* workspace,
+              size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (T < 0 || top_k < 1 || E < 1 || E > 1024)
+    return fail(MOE_ERR_INVALID_ARG, "T=%d top_k=%d E=%d", T, top_k, E);
+  if (!valid_block_m(block_m)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", block_m);
+  if (static_cast<int64_t>(T) * top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
+  if (!expert_counts || !expert_offsets || !num_tokens_post_padded || (T > 0 && !topk_ids) ||
+      (T > 0 && (!sorted_token_ids || !block_expert_ids)))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  const size_t need = moe_align_workspace_bytes(T, top_k, E, block_m);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "align workspace %zu < %zu", workspace_bytes, need);
+  const Caps c = capacities(T, top_k, E, block_m);
+  moe::launch_align(topk_ids, static_cast<int64_t>(T) * top_k, E, block_m, expert_counts,
+                    expert_offsets, sorted_token_ids, c.sorted_cap, block_expert_ids, c.block_cap,
+                    num_tokens_post_padded, workspace, stream);
+  return check_launch("moe_align");
+}
+
+size_t moe_experts_workspace_bytes(int T, int H, int top_k, const moe_weights* weights,
+                                   int activation, int block_m) {
+  if (!weights || T < 0 || top_k < 1 || !valid_block_m(block_m)) return 0;
+  if (check_weights(weights, H, activation, false) != MOE_OK) return 0;
+  Carve c(nullptr);
+  void *z, *zsh;
+  float *zs, *zshs;
+  return experts_ws(T, top_k, weights, block_m, c, &z, &zs, &zsh, &zshs);
+}
+
+int moe_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
+                const float* shared_in_scale, int T, int H, int top_k,
+                const moe_weights* weights, int activation, const int32_t* sorted_token_ids,
+                const int32_t* block_expert_ids, const int32_t* num_tokens_post_padded,
+                int block_m, uint16_t* fused_expert_output, uint16_t* shared_out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (T < 0 || top_k < 1) return fail(MOE_ERR_INVALID_ARG, "T=%d top_k=%d", T, top_k);
+  if (!valid_block_m(block_m)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", block_m);
+  if (int st = check_weights(weights, H, activation, true)) return st;
+  if (top_k > weights->num_experts) return fail(MOE_ERR_INVALID_ARG, "top_k > E");
+  const bool fp8 = weights->quant == MOE_QUANT_FP8_G128;
+  if (fp8 && block_m > 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts support block_m <= 128");
+  if (static_cast<int64_t>(T) * top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
+  if (T == 0) return MOE_OK;
+  if (!a1q || !sorted_token_ids || !block_expert_ids || !num_tokens_post_padded ||
+      !fused_expert_output || (fp8 && !a1q_scale))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (weights->shared_inter > 0 && (!shared_in || !shared_out || (fp8 && !shared_in_scale)))
+    return fail(MOE_ERR_INVALID_ARG, "shared expert needs shared_in (+scale) and shared_out");
+  const size_t need = moe_experts_workspace_bytes(T, H, top_k, weights, activation, block_m);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "experts workspace %zu < %zu", workspace_bytes, need);
+  return run_experts(a1q, a1q_scale, shared_in, shared_in_scale, T, H, top_k, weights, activation,
+                     sorted_token_ids, block_expert_ids, num_tokens_post_padded, block_m,
+                     fused_expert_output, shared_out, workspace, StageEvents{nullptr, stream},
+                     stream);
+}
+
+int moe_finalize(void* output, float* output_scale, int out_quant,
+                 const uint16_t* fused_expert_output, const float* topk_weights,
+                 const int32_t* topk_ids, int T, int top_k, int H,
+                 int apply_router_weight_on_input, const uint16_t* shared,
+                 const uint16_t* residual, uint16_t* residual_out, const uint16_t* gamma,
+                 float eps, hipStream_t stream) {
+  g_err[0] = 0;
+  (void)topk_ids;
+  if (T < 0 || top_k < 1 || top_k > 64) return fail(MOE_ERR_INVALID_ARG, "T=%d top_k=%d", T, top_k);
+  if (H <= 0 || H % 8 || H > 16384) return fail(MOE_ERR_INVALID_ARG, "H=%d", H);
+  if (out_quant != MOE_QUANT_NONE && out_quant != MOE_QUANT_FP8_G128)
+    return fail(MOE_ERR_UNSUPPORTED, "out_quant %d", out_quant);
+  if (out_quant == MOE_QUANT_FP8_G128 && H % 128)
+    return fail(MOE_ERR_INVALID_ARG, "fp8 output needs H %% 128 == 0");
+  if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+  if (T == 0) return MOE_OK;
+  if (!output || !fused_expert_output || (!apply_router_weight_on_input && !topk_weights) ||
+      (out_quant == MOE_QUANT_FP8_G128 && !output_scale))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  moe::launch_finalize(output, output_scale, out_quant, fused_expert_output, topk_weights, T, top_k,
+                       H, apply_router_weight_on_input ? 1 : 0, shared, residual, residual_out,
+                       gamma, eps, stream);
+  return check_launch("moe_finalize");
+}
+
+namespace {
+
+struct ForwardLayout {
+  int32_t* ids;
+  float* tw;
+  void* a1q;
+  float* a1q_scale;
+  void* shin;
+  float* shin_scale;
+  int32_t *counts, *offsets, *sorted, *blocks, *ntp;
+  void* align_ws;
+  void* experts_ws;
+  size_t experts_ws_bytes;
+  uint16_t* feo;
+  uint16_t* shared_out;
+};
+
+size_t forward_layout(int T, int H, int top_k, const moe_weights* w, int bm, int woi,
+                      void* base, ForwardLayout* L) {
+  Carve c(base);
+  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const size_t eb = fp8 ? 1 : 2;
+  const int E = w->num_experts;
+  const int64_t n = static_cast<int64_t>(T) * top_k;
+  const Caps cp = capacities(T, top_k, E, bm);
+  L->ids = static_cast<int32_t*>(c.take(n * 4));
+  L->tw = static_cast<float*>(c.take(n * 4));
+  L->a1q = c.take(static_cast<size_t>(T) * H * eb);
+  L->a1q_scale = fp8 ? static_cast<float*>(c.take(static_cast<size_t>(T) * (H / 128) * 4)) : nullptr;
+  L->shin = nullptr;
+  L->shin_scale = nullptr;
+  if (w->shared_inter > 0 && woi && fp8) {
+    L->shin = c.take(static_cast<size_t>(T) * H);
+    L->shin_scale = static_cast<float*>(c.take(static_cast<size_t>(T) * (H / 128) * 4));
+  }
+  L->counts = static_cast<int32_t*>(c.take(E * 4));
+  L->offsets = static_cast<int32_t*>(c.take((E + 1) * 4));
+  L->sorted = static_cast<int32_t*>(c.take(cp.sorted_cap * 4));
+  L->blocks = static_cast<int32_t*>(c.take(cp.block_cap * 4));
+  L->ntp = static_cast<int32_t*>(c.take(4));
+  L->align_ws = c.take(moe::align_workspace_bytes(n, E));
+  Carve sub(nullptr);
+  void *z, *zsh;
+  float *zs, *zshs;
+  L->experts_ws_bytes = experts_ws(T, top_k, w, bm, sub, &z, &zs, &zsh, &zshs);
+  L->experts_ws = c.take(L->experts_ws_bytes);
+  L->feo = static_cast<uint16_t*>(c.take(static_cast<size_t>(n) * H * 2));
+  L->shared_out = w->shared_inter > 0 ? static_cast<uint16_t*>(c.take(static_cast<size_t>(T) * H * 2))
+                                      : nullptr;
+  return c.used;
+}
+
+}  // namespace
+
+size_t moe_forward_workspace_bytes(int T, int H, int top_k, const moe_weights* weights,
+                                   int activation, int block_m, int apply_router_weight_on_input) {
+  if (!weights || T < 0 || top_k < 1) return 0;
+  if (check_weights(weights, H, activation, false) != MOE_OK) return 0;
+  const int bm = block_m ? block_m : moe_pick_block_m(T, top_k, weights->num_experts);
+  if (!valid_block_m(bm)) return 0;
+  ForwardLayout L;
+  return forward_layout(T, H, top_k, weights, bm, apply_router_weight_on_input, nullptr, &L);
+}
+
+int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k, int scoring,
+                int renormalize, int apply_router_weight_on_input, const moe_weights* weights,
+                int activation, int block_m, const uint16_t* residual, const uint16_t* gamma,
+                float eps, int out_quant, void* output, float* output_scale,
+                uint16_t* residual_out, void* workspace, size_t workspace_bytes,
+                hipEvent_t* stage_events, hipStream_t stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+  if (int st = check_weights(weights, H, activation, true)) return st;
+  const int E = weights->num_experts;
+  if (top_k < 1 || top_k > std::min(E, 64)) return fail(MOE_ERR_INVALID_ARG, "top_k=%d", top_k);
+  if (scoring != MOE_SCORING_SOFTMAX && scoring != MOE_SCORING_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "scoring=%d", scoring);
+  if (apply_router_weight_on_input && top_k != 1)
+    return fail(MOE_ERR_INVALID_ARG, "router weight on the input needs top_k == 1");
+  if (out_quant != MOE_QUANT_NONE && out_quant != MOE_QUANT_FP8_G128)
+    return fail(MOE_ERR_UNSUPPORTED, "out_quant %d", out_quant);
+  if (H > 16384) return fail(MOE_ERR_INVALID_ARG, "H=%d > 16384", H);
+  if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+  if (static_cast<int64_t>(T) * top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
+  const int bm = block_m ? block_m : moe_pick_block_m(T, top_k, E);
+  if (!valid_block_m(bm)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", bm);
+  const bool fp8 = weights->quant == MOE_QUANT_FP8_G128;
+  if (fp8 && bm > 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts support block_m <= 128");
+  if (T == 0) return MOE_OK;
+  if (!x || !logits || !output || (out_quant == MOE_QUANT_FP8_G128 && !output_scale))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  ForwardLayout L;
+  const size_t need = forward_layout(T, H, top_k, weights, bm, apply_router_weight_on_input,
+                                     nullptr, &L);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "forward workspace %zu < %zu", workspace_bytes, need);
+  forward_layout(T, H, top_k, weights, bm, apply_router_weight_on_input, workspace, &L);
+  const StageEvents se{stage_events, stream};
+  const int quant = weights->quant;
+  const int64_t n = static_cast<int64_t>(T) * top_k;
+  const Caps cp = capacities(T, top_k, E, bm);
+
+  se.mark(0);
+  moe::launch_route(logits, T, E, top_k, scoring, renormalize ? 1 : 0, L.ids, L.tw, stream);
+  se.mark(1);
+  const void* a1q = x;
+  if (quant == MOE_QUANT_FP8_G128 || apply_router_weight_on_input) {
+    moe::launch_prepare(x, T, H, L.tw, apply_router_weight_on_input ? 1 : 0, quant, L.a1q,
+                        L.a1q_scale, stream);
+    a1q = L.a1q;
+  }
+  // The shared expert reads the unweighted input in a1q's format.
+  const void* shin = a1q;
+  const float* shin_scale = L.a1q_scale;
+  if (weights->shared_inter > 0 && apply_router_weight_on_input) {
+    if (fp8) {
+      moe::launch_prepare(x, T, H, nullptr, 0, quant, L.shin, L.shin_scale, stream);
+      shin = L.shin;
+      shin_scale = L.shin_scale;
+    } else {
+      shin = x;
+      shin_scale = nullptr;
+    }
+  }
+  se.mark(2);
+  moe::launch_align(L.ids, n, E, bm, L.counts, L.offsets, L.sorted, cp.sorted_cap, L.blocks,
+                    cp.block_cap, L.ntp, L.align_ws, stream);
+  se.mark(3);
+  int st = run_experts(a1q, L.a1q_scale, shin, shin_scale, T, H, top_k, weights, activation,
+                       L.sorted, L.blocks, L.ntp, bm, L.feo, L.shared_out, L.experts_ws, se, stream);
+  if (st) return st;
+  moe::launch_finalize(output, output_scale, out_quant, L.feo, L.tw, T, top_k, H,
+                       apply_router_weight_on_input ? 1 : 0, L.shared_out, residual, residual_out,
+                       gamma, eps, stream);
+  se.mark(7);
+  return check_launch("moe_forward");
+}
+
+}  // extern "C"

@@ -1,0 +1,227 @@
+"""GPU parity of the experts stage and the whole layer (moe_forward) against
+the CPU oracle: reduced cases element by element, the five workload families
+at their full sizes on sampled tokens (route and align checked in full)."""
+
+import gc
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, PARITY_CASES, make_layer_inputs, to_numpy_bits
+from helpers import check_tolerance, f64_of_bf16, f64_of_fp8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+WKEYS = ("w13", "w13_scale", "w2", "w2_scale", "shared_w13", "shared_w13_scale", "shared_w2",
+         "shared_w2_scale")
+
+
+def _moe():
+    import mixture_experts_layer_routing_amd as moe
+    return moe
+
+
+def _announce(name):
+    print(f"[case] {name}", file=sys.stderr, flush=True)
+
+
+def _weights(moe, d):
+    return moe.make_weights(*(d.get(k) for k in ("w13", "w2", "w13_scale", "w2_scale", "shared_w13",
+                                                 "shared_w2", "shared_w13_scale", "shared_w2_scale")))
+
+
+def _host_w(d):
+    return {k: to_numpy_bits(d[k]) for k in WKEYS if d.get(k) is not None}
+
+
+def _out_f64(spec, out, scale, sel=slice(None)):
+    if spec.out_quant == "fp8":
+        return f64_of_fp8(to_numpy_bits(out)[sel], scale.cpu().numpy()[sel])
+    return f64_of_bf16(to_numpy_bits(out)[sel])
+
+
+def _ref_f64(spec, r):
+    if spec.out_quant == "fp8":
+        return f64_of_fp8(r["output"], r["output_scale"])
+    return f64_of_bf16(r["output"])
+
+
+def _path(spec):
+    return "fp8" if (spec.quant == "fp8" or spec.out_quant == "fp8") else "bf16"
+
+
+# ------------------------------------------------------ experts stage, reduced
+@pytest.mark.parametrize("spec", PARITY_CASES, ids=lambda s: s.name)
+@pytest.mark.parametrize("BM", [16, 64, 128])
+def test_experts_stage_reduced(spec, BM):
+    _announce(f"experts {spec.name} BM={BM}")
+    moe = _moe()
+    d = make_layer_inputs(spec)
+    dd = {k: v.to(DEV) for k, v in d.items()}
+    rid, rw = oracle.route(d["logits"].numpy(), spec.top_k, spec.scoring, spec.renormalize)
+    x_bits = to_numpy_bits(d["x"])
+    ra, rs = oracle.prepare(x_bits, rw, spec.apply_router_weight_on_input, spec.quant)
+    ids = torch.from_numpy(rid).to(DEV)
+    tw = torch.from_numpy(rw).to(DEV)
+    a1q, a1s = moe.moe_prepare(dd["x"], tw, spec.apply_router_weight_on_input, spec.quant)
+    sh_in, sh_s = None, None
+    shared = None
+    if spec.shared_I:
+        if spec.apply_router_weight_on_input:
+            sh_in, sh_s = moe.moe_prepare(dd["x"], None, False, spec.quant)
+            sa, ss = oracle.prepare(x_bits, None, False, spec.quant)
+        else:
+            sa, ss = ra, rs
+        hw = _host_w(d)
+        shared = dict(a=sa, a_scale=ss, w13=hw["shared_w13"], w13_scale=hw.get("shared_w13_scale"),
+                      w2=hw["shared_w2"], w2_scale=hw.get("shared_w2_scale"))
+    al = moe.moe_align(ids, spec.E, BM)
+    w = _weights(moe, dd)
+    feo, sho = moe.moe_experts(a1q, a1s, w, spec.top_k, al, BM, spec.activation, sh_in, sh_s)
+    torch.cuda.synchronize()
+    hw = _host_w(d)
+    refs = {}
+    for mode in ("exact", "mirrored"):
+        refs[mode] = oracle.experts(ra, rs, rid, hw["w13"], hw.get("w13_scale"), hw["w2"],
+                                    hw.get("w2_scale"), spec.activation, mode, shared)
+    path = "fp8" if spec.quant == "fp8" else "bf16"
+    check_tolerance(f64_of_bf16(feo), f64_of_bf16(refs["exact"][0]), f64_of_bf16(refs["mirrored"][0]),
+                    path, f"{spec.name} fused_expert_output")
+    if spec.shared_I:
+        check_tolerance(f64_of_bf16(sho), f64_of_bf16(refs["exact"][1]),
+                        f64_of_bf16(refs["mirrored"][1]), path, f"{spec.name} shared_out")
+
+
+# ------------------------------------------------------- whole layer, reduced
+def _forward_block_ms(spec):
+    return [0, 16, 32, 64, 128] + ([256] if spec.quant == "none" else [])
+
+
+@pytest.mark.parametrize("spec", PARITY_CASES, ids=lambda s: s.name)
+def test_forward_reduced(spec):
+    moe = _moe()
+    d = make_layer_inputs(spec)
+    dd = {k: v.to(DEV) for k, v in d.items()}
+    w = _weights(moe, dd)
+    hw = _host_w(d)
+    refs = {mode: oracle.forward(to_numpy_bits(d["x"]), d["logits"].numpy(), hw, spec.top_k,
+                                 spec.scoring, spec.renormalize, 16,
+                                 spec.apply_router_weight_on_input, spec.quant, spec.activation,
+                                 mode, to_numpy_bits(d.get("residual")), to_numpy_bits(d.get("gamma")),
+                                 spec.eps, spec.out_quant)
+            for mode in ("exact", "mirrored")}
+    for bm in _forward_block_ms(spec):
+        _announce(f"forward {spec.name} BM={bm}")
+        out, scale, _ = moe.moe_forward(dd["x"], dd["logits"], w, spec.top_k, spec.scoring,
+                                        spec.renormalize, spec.apply_router_weight_on_input,
+                                        spec.activation, bm, dd.get("residual"), dd.get("gamma"),
+                                        spec.eps, spec.out_quant)
+        torch.cuda.synchronize()
+        check_tolerance(_out_f64(spec, out, scale), _ref_f64(spec, refs["exact"]),
+                        _ref_f64(spec, refs["mirrored"]), _path(spec), f"{spec.name} BM={bm}")
+
+
+def test_forward_zero_tokens_is_a_no_op():
+    moe = _moe()
+    spec = PARITY_CASES[1]
+    d = {k: v.to(DEV) for k, v in make_layer_inputs(spec).items()}
+    w = _weights(moe, d)
+    x = torch.empty((0, spec.H), dtype=torch.bfloat16, device=DEV)
+    lg = torch.empty((0, spec.E), dtype=torch.float32, device=DEV)
+    out, _, _ = moe.moe_forward(x, lg, w, spec.top_k)
+    torch.cuda.synchronize()
+    assert out.shape == (0, spec.H)
+
+
+def test_forward_token_permutation_equivariance():
+    """Permuting the tokens permutes the output rows bit-for-bit (rows are
+    independent and every per-row reduction order is fixed)."""
+    moe = _moe()
+    spec = PARITY_CASES[1]
+    d = {k: v.to(DEV) for k, v in make_layer_inputs(spec).items()}
+    w = _weights(moe, d)
+    perm = torch.randperm(spec.T, generator=torch.Generator().manual_seed(0)).to(DEV)
+    a, _, _ = moe.moe_forward(d["x"], d["logits"], w, spec.top_k, spec.scoring, spec.renormalize,
+                              block_m=16)
+    b, _, _ = moe.moe_forward(d["x"][perm].contiguous(), d["logits"][perm].contiguous(), w,
+                              spec.top_k, spec.scoring, spec.renormalize, block_m=16)
+    torch.cuda.synchronize()
+    assert torch.equal(a[perm].view(torch.int16), b.view(torch.int16))
+
+
+def test_forward_unit_weight_on_input_matches_no_flag():
+    """With top-1 softmax renormalised the router weight is exactly 1, so
+    putting it on the input changes nothing: bit-identical outputs."""
+    moe = _moe()
+    spec = PARITY_CASES[3]
+    d = {k: v.to(DEV) for k, v in make_layer_inputs(spec).items()}
+    w = _weights(moe, d)
+    a, _, _ = moe.moe_forward(d["x"], d["logits"], w, 1, "softmax", True, True)
+    b, _, _ = moe.moe_forward(d["x"], d["logits"], w, 1, "softmax", True, False)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------------ full sizes, sampled tokens
+_CACHE = {}
+
+
+def _full_inputs(spec):
+    """Weights are drawn once per family (they do not depend on T)."""
+    fam = (spec.config, spec.activation)
+    if _CACHE.get("fam") != fam:
+        _CACHE.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+        d = make_layer_inputs(spec, device=DEV)
+        _CACHE["fam"] = fam
+        _CACHE["dev"] = {k: d[k] for k in WKEYS if d.get(k) is not None}
+        _CACHE["host"] = {k: to_numpy_bits(v) for k, v in _CACHE["dev"].items()}
+    d = make_layer_inputs(spec, device=DEV, weights=False)
+    d.update(_CACHE["dev"])
+    return d, _CACHE["host"]
+
+
+def _full_cases():
+    out = []
+    for fam in ("tiny", "mixtral", "deepseek_v3", "llama4"):
+        out += CONFIGS[fam]
+    return out
+
+
+@pytest.mark.parametrize("spec", _full_cases(), ids=lambda s: s.name)
+def test_forward_full_size_sampled(spec):
+    _announce(f"full {spec.name}")
+    moe = _moe()
+    d, hw = _full_inputs(spec)
+    w = _weights(moe, d)
+    bm = moe.moe_pick_block_m(spec.T, spec.top_k, spec.E)
+    out, scale, _ = moe.moe_forward(d["x"], d["logits"], w, spec.top_k, spec.scoring,
+                                    spec.renormalize, spec.apply_router_weight_on_input,
+                                    spec.activation, 0, d.get("residual"), d.get("gamma"), spec.eps,
+                                    spec.out_quant)
+    ids, _ = moe.moe_route(d["logits"], spec.top_k, spec.scoring, spec.renormalize)
+    al = moe.moe_align(ids, spec.E, bm)
+    torch.cuda.synchronize()
+    logits = d["logits"].cpu().numpy()
+    rid, _ = oracle.route(logits, spec.top_k, spec.scoring, spec.renormalize)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    ral = oracle.align(rid, spec.E, bm)
+    for k in ("expert_counts", "expert_offsets", "sorted_token_ids", "block_expert_ids"):
+        np.testing.assert_array_equal(al[k].cpu().numpy(), ral[k], err_msg=k)
+    n = min(spec.T, 6 if spec.E > 64 else 8)
+    rng = np.random.default_rng(spec.T)
+    sample = np.sort(rng.choice(spec.T, size=n, replace=False))
+    sample[-1] = spec.T - 1
+    x_bits = to_numpy_bits(d["x"])
+    refs = {mode: oracle.forward(x_bits, logits, hw, spec.top_k, spec.scoring, spec.renormalize, bm,
+                                 spec.apply_router_weight_on_input, spec.quant, spec.activation,
+                                 mode, to_numpy_bits(d.get("residual")), to_numpy_bits(d.get("gamma")),
+                                 spec.eps, spec.out_quant, tokens=sample)
+            for mode in ("exact", "mirrored")}
+    got = _out_f64(spec, out, scale, sample)
+    check_tolerance(got, _ref_f64(spec, refs["exact"]), _ref_f64(spec, refs["mirrored"]),
+                    _path(spec), spec.name)
