@@ -194,6 +194,19 @@ int moe_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
 /* (host) workspace moe_experts needs. */
 size_t moe_experts_workspace_bytes(int T, int H, int top_k, const moe_weights* weights,
                                    int activation, int block_m);
+/*
+ * (host) Where moe_experts keeps the intermediate activation z inside its
+ * workspace.  z stays there after the call until the workspace is reused,
+ * so a caller can inspect what the second GEMM consumed.  out[5] receives
+ * byte offsets from the workspace start (SIZE_MAX when absent):
+ *   out[0] z of the routed rows, [rows, I] bf16 (E4M3 codes for fp8); row r
+ *          belongs to flat row sorted_token_ids[r] (pad rows hold act(0))
+ *   out[1] its G(128) scales [rows, I/128] fp32 (fp8 only)
+ *   out[2] z of the shared expert [T, I_s]   out[3] its scales (fp8 only)
+ *   out[4] rows = block capacity * block_m (a count, not an offset)
+ */
+int moe_experts_workspace_layout(int T, int H, int top_k, const moe_weights* weights,
+                                 int activation, int block_m, size_t* out);
 
 /*
  * moe_finalize -- the no-DP/EP finalize (weight-and-reduce over the top-k

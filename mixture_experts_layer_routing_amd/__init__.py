@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     moe_align,
     moe_align_capacity,
     moe_experts,
+    moe_experts_workspace_layout,
     moe_finalize,
     moe_forward,
     moe_forward_workspace_bytes,

@@ -47,7 +47,7 @@ class MoeError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m mixture_experts_layer_routing_amd.build`")
+                          "`python mixture_experts_layer_routing_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     sig = {
         "moe_status_str": (ctypes.c_char_p, [c_int]),
@@ -65,6 +65,8 @@ def _load():
                                 c_vp, c_vp, c_vp, c_sz, c_vp]),
         "moe_experts_workspace_bytes": (c_sz, [c_int, c_int, c_int, ctypes.POINTER(MoeWeights),
                                                c_int, c_int]),
+        "moe_experts_workspace_layout": (c_int, [c_int, c_int, c_int, ctypes.POINTER(MoeWeights),
+                                                 c_int, c_int, ctypes.POINTER(c_sz)]),
         "moe_finalize": (c_int, [c_vp, c_vp, c_int, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                  c_vp, c_vp, c_vp, c_vp, c_f32, c_vp]),
         "moe_forward": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
@@ -191,7 +193,10 @@ def moe_align(topk_ids, E, block_m, stream=None):
 
 def moe_experts(a1q, a1q_scale, weights, top_k, align_out, block_m, activation="silu",
                 shared_in=None, shared_in_scale=None, fused_expert_output=None, shared_out=None,
-                stream=None):
+                workspace=None, stream=None):
+    """Returns (fused_expert_output, shared_out); with ``workspace`` given
+    (a uint8 tensor) the intermediate z stays readable in it afterwards
+    (see moe_experts_workspace_layout)."""
     T, H = a1q.shape
     dev = a1q.device
     if fused_expert_output is None:
@@ -200,7 +205,9 @@ def moe_experts(a1q, a1q_scale, weights, top_k, align_out, block_m, activation="
         shared_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     act = ACTIVATION[activation]
     wsb = _lib.moe_experts_workspace_bytes(T, H, top_k, ctypes.byref(weights), act, block_m)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ws = workspace
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     if weights.shared_inter > 0 and shared_in is None:
         shared_in, shared_in_scale = a1q, a1q_scale
     _check(_lib.moe_experts(_ptr(a1q), _ptr(a1q_scale), _ptr(shared_in), _ptr(shared_in_scale), T, H,
@@ -210,6 +217,18 @@ def moe_experts(a1q, a1q_scale, weights, top_k, align_out, block_m, activation="
                             _ptr(fused_expert_output), _ptr(shared_out), _ptr(ws), wsb,
                             _stream(stream)), "moe_experts")
     return fused_expert_output, shared_out
+
+
+def moe_experts_workspace_layout(T, H, top_k, weights, activation="silu", block_m=16):
+    """Byte offsets of the intermediate z (and scales) inside moe_experts'
+    workspace: dict(z, z_scale, shared_z, shared_z_scale, rows); None = absent."""
+    out = (c_sz * 5)()
+    _check(_lib.moe_experts_workspace_layout(T, H, top_k, ctypes.byref(weights),
+                                             ACTIVATION[activation], block_m, out),
+           "moe_experts_workspace_layout")
+    none = (1 << (8 * ctypes.sizeof(c_sz))) - 1
+    v = [None if x == none else x for x in out]
+    return dict(z=v[0], z_scale=v[1], shared_z=v[2], shared_z_scale=v[3], rows=v[4])
 
 
 def moe_finalize(fused_expert_output, topk_weights, topk_ids=None,
@@ -257,6 +276,11 @@ def moe_forward(x, logits, weights, top_k, scoring="softmax", renormalize=True,
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     ev = None
     if stage_events is not None:
+        if len(stage_events) != NUM_STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {NUM_STAGE_EVENTS} events")
+        for e in stage_events:
+            if e.cuda_event == 0:      # torch creates the HIP event on its first record
+                e.record(stream if stream is not None else torch.cuda.current_stream())
         ev = (c_vp * NUM_STAGE_EVENTS)(*[e.cuda_event for e in stage_events])
     _check(_lib.moe_forward(_ptr(x), _ptr(logits), T, H, top_k, SCORING[scoring], int(renormalize),
                             int(apply_router_weight_on_input), ctypes.byref(weights),

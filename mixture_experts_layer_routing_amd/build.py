@@ -1,6 +1,6 @@
 """Build libmoe.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m mixture_experts_layer_routing_amd.build [--jobs N]
+Usage: python mixture_experts_layer_routing_amd/build.py [--jobs N]
 Every call recompiles every source (it is also the "does it build" check).
 """
 

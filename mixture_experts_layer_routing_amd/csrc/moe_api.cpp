@@ -32,13 +32,16 @@ int check_launch(const char* what) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Bump allocator over the caller's workspace (sizes only when base is null).
+// Bump allocator over the caller's workspace (sizes only when base is null);
+// `last` is the byte offset of the most recent piece.
 struct Carve {
   char* base;
   size_t used = 0;
+  size_t last = 0;
   explicit Carve(void* b) : base(static_cast<char*>(b)) {}
   void* take(size_t bytes) {
     void* p = base ? base + used : nullptr;
+    last = used;
     used += align_up(bytes);
     return p;
   }
@@ -95,20 +98,32 @@ int check_weights(const moe_weights* w, int H, int activation, bool need_ptrs) {
 // Workspace of the experts stage: z for the routed rows and for the shared
 // expert, in the GEMM input format of the second GEMM.
 size_t experts_ws(int T, int top_k, const moe_weights* w, int bm, Carve& c, void** z,
-                  float** zs, void** zsh, float** zshs) {
+                  float** zs, void** zsh, float** zshs, size_t* offs = nullptr) {
   const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
   const size_t eb = fp8 ? 1 : 2;
   const Caps cp = capacities(T, top_k, w->num_experts, bm);
   const int64_t rows = cp.block_cap * bm;
   const size_t start = c.used;
+  const size_t none = static_cast<size_t>(-1);
+  size_t o[5] = {none, none, none, none, static_cast<size_t>(rows)};
   *z = c.take(static_cast<size_t>(rows) * w->inter * eb);
-  *zs = fp8 ? static_cast<float*>(c.take(static_cast<size_t>(rows) * (w->inter / 128) * 4)) : nullptr;
+  o[0] = c.last - start;
+  *zs = nullptr;
+  if (fp8) {
+    *zs = static_cast<float*>(c.take(static_cast<size_t>(rows) * (w->inter / 128) * 4));
+    o[1] = c.last - start;
+  }
   *zsh = nullptr;
   *zshs = nullptr;
   if (w->shared_inter > 0) {
     *zsh = c.take(static_cast<size_t>(T) * w->shared_inter * eb);
-    if (fp8) *zshs = static_cast<float*>(c.take(static_cast<size_t>(T) * (w->shared_inter / 128) * 4));
+    o[2] = c.last - start;
+    if (fp8) {
+      *zshs = static_cast<float*>(c.take(static_cast<size_t>(T) * (w->shared_inter / 128) * 4));
+      o[3] = c.last - start;
+    }
   }
+  if (offs) for (int i = 0; i < 5; ++i) offs[i] = o[i];
   return c.used - start;
 }
 
@@ -329,6 +344,19 @@ size_t moe_experts_workspace_bytes(int T, int H, int top_k, const moe_weights* w
   void *z, *zsh;
   float *zs, *zshs;
   return experts_ws(T, top_k, weights, block_m, c, &z, &zs, &zsh, &zshs);
+}
+
+int moe_experts_workspace_layout(int T, int H, int top_k, const moe_weights* weights,
+                                 int activation, int block_m, size_t* out) {
+  g_err[0] = 0;
+  if (!out || T < 0 || top_k < 1 || !valid_block_m(block_m))
+    return fail(MOE_ERR_INVALID_ARG, "bad arguments");
+  if (int st = check_weights(weights, H, activation, false)) return st;
+  Carve c(nullptr);
+  void *z, *zsh;
+  float *zs, *zshs;
+  experts_ws(T, top_k, weights, block_m, c, &z, &zs, &zsh, &zshs, out);
+  return MOE_OK;
 }
 
 int moe_experts(const void* a1q, const float* a1q_scale, const void* shared_in,

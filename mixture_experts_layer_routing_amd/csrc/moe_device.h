@@ -84,8 +84,10 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// silu(v) = v / (1 + exp(-v)) with the accurate expf: on the fp8 path z is
+// re-quantised, and a closer z flips fewer codes at rounding edges.
 __device__ __forceinline__ float silu(float v) {
-  return v / (1.0f + __expf(-v));
+  return v / (1.0f + expf(-v));
 }
 
 }  // namespace moe

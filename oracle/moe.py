@@ -223,22 +223,32 @@ def _round_intermediate(z, mode, quant):
     return bf16_bits_to_f64(f64_to_bf16_bits(z))
 
 
-def expert_mlp(a, w13, w2, activation="silu", mode="exact", quant="none"):
-    """One expert on rows ``a`` [n, H] (float64) with dequantised
-    W13 [2I or I, H] and W2 [H, I] (float64).  Matmul is the library
-    primitive; accumulation is float64."""
+def expert_gemm1(a, w13, activation="silu"):
+    """First half of one expert on rows ``a`` [n, H] (float64) with the
+    dequantised W13 [2I or I, H]: h = a W13^T (library matmul, float64),
+    then the activation.  Returns z [n, I] (float64, unrounded)."""
     h = a @ w13.T
     if callable(activation):        # a test-only activation without a gate/up split
-        z = activation(h)
-    elif activation == "silu":
+        return activation(h)
+    if activation == "silu":
         inter = w13.shape[0] // 2
-        z = silu(h[:, :inter]) * h[:, inter:]
-    elif activation == "silu_no_mul":
-        z = silu(h)
-    else:
-        raise ValueError(activation)
-    z = _round_intermediate(z, mode, quant)
+        return silu(h[:, :inter]) * h[:, inter:]
+    if activation == "silu_no_mul":
+        return silu(h)
+    raise ValueError(activation)
+
+
+def expert_gemm2(z, w2):
+    """Second half: y = z W2^T with the dequantised W2 [H, I] (float64)."""
     return z @ w2.T
+
+
+def expert_mlp(a, w13, w2, activation="silu", mode="exact", quant="none"):
+    """One expert: y = W2 act(W13 a), with z rounded where the kernels store
+    it when mode == "mirrored"."""
+    z = expert_gemm1(a, w13, activation)
+    z = _round_intermediate(z, mode, quant)
+    return expert_gemm2(z, w2)
 
 
 def experts(a1q, a1q_scale, topk_ids, w13, w13_scale, w2, w2_scale,

@@ -28,9 +28,15 @@ def f64_of_fp8(codes, scales):
     return codecs.e4m3_decode(codes) * np.repeat(np.asarray(scales, np.float64), 128, axis=-1)
 
 
-def check_tolerance(got, ref_exact, ref_mirrored, path, what=""):
+def check_tolerance(got, ref_exact, ref_mirrored, path, what="", elementwise=True):
     """The parity bar for floating-point outputs: max-norm bound against both
-    oracle modes, per-element relative bound against the mirrored mode."""
+    oracle modes, per-element relative bound against the mirrored mode.
+
+    elementwise=False drops the per-element bound: used for end-to-end
+    outputs downstream of the fp8 re-quantisation of the intermediate z,
+    where two correct results legitimately differ by whole fp8 code steps at
+    rounding edges; there the per-element bound is checked stage by stage
+    (z codes within one step, GEMM-2 against the z it consumed)."""
     bound = BF16_BOUND if path == "bf16" else FP8_BOUND
     got = np.asarray(got, np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
@@ -43,7 +49,7 @@ def check_tolerance(got, ref_exact, ref_mirrored, path, what=""):
         err = np.abs(got - ref).max() if ref.size else 0.0
         report[name] = err / m if m > 0 else err
         assert err <= bound * m + 1e-30, f"{what}: max|err| {err:.3g} > {bound} * max|ref| {m:.3g} ({name})"
-    if ref_mirrored is not None and np.asarray(ref_mirrored).size:
+    if elementwise and ref_mirrored is not None and np.asarray(ref_mirrored).size:
         ref = np.asarray(ref_mirrored, np.float64)
         mask = np.abs(ref) > ELEM_FLOOR
         if mask.any():
@@ -55,3 +61,37 @@ def check_tolerance(got, ref_exact, ref_mirrored, path, what=""):
 
 def np_bits(t):
     return to_numpy_bits(t)
+
+
+def e4m3_step(v):
+    """Distance from |v| (an E4M3 value) to its next code up: 2^-9 below 2^-6,
+    else 2^(floor(log2 |v|) - 3)."""
+    a = np.abs(np.asarray(v, np.float64))
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))
+    return np.ldexp(1.0, ex - 1 - 3)
+
+
+# The kernel's z is an fp32 sum over H with per-128 block-scale promotions,
+# accumulated inside the fp8 matrix unit in its own order; measured on the
+# MI355X its absolute error reaches ~3.5e-5 of the group's amax (an fp32
+# emulation of the same blocking stays below 3e-7).  Codes near zero may
+# therefore differ by up to 1e-4 * amax = 0.0448 code units (448 units =
+# amax), i.e. ~23 E4M3 subnormal steps; larger codes by one step.
+Z_CODE_FLOOR = 1e-4 * 448.0
+
+
+def check_fp8_codes(q_got, s_got, z_ref, what=""):
+    """GPU E4M3 G(128) codes/scales of an fp32 quantity against the oracle's
+    quantisation of its own float64 value: scales agree to 1e-4, and each
+    code is the oracle's, its neighbour (the values straddled a rounding
+    edge), or -- near zero -- within the fp32 accumulation floor.  Returns
+    the fraction of identical codes."""
+    import oracle
+    q_ref, s_ref = oracle.quantize_g128(z_ref)
+    np.testing.assert_allclose(s_got, s_ref, rtol=1e-4, err_msg=f"{what}: z scales")
+    vg = codecs.e4m3_decode(q_got)
+    vr = codecs.e4m3_decode(q_ref)
+    tol = np.maximum(e4m3_step(np.maximum(np.abs(vg), np.abs(vr))), Z_CODE_FLOOR) + 1e-12
+    bad = np.abs(vg - vr) > tol
+    assert not bad.any(), f"{what}: {bad.sum()} z codes beyond one step / the accumulation floor"
+    return float((q_got == q_ref).mean())

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from workloads import CONFIGS, PARITY_CASES, make_layer_inputs, to_numpy_bits
-from helpers import check_tolerance, f64_of_bf16, f64_of_fp8
+from helpers import check_tolerance, check_fp8_codes, f64_of_bf16, f64_of_fp8
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -80,19 +80,69 @@ def test_experts_stage_reduced(spec, BM):
                       w2=hw["shared_w2"], w2_scale=hw.get("shared_w2_scale"))
     al = moe.moe_align(ids, spec.E, BM)
     w = _weights(moe, dd)
-    feo, sho = moe.moe_experts(a1q, a1s, w, spec.top_k, al, BM, spec.activation, sh_in, sh_s)
+    ws = torch.empty(moe.binding.lib().moe_experts_workspace_bytes(
+        spec.T, spec.H, spec.top_k, moe.binding.ctypes.byref(w),
+        moe.binding.ACTIVATION[spec.activation], BM), dtype=torch.uint8, device=DEV)
+    feo, sho = moe.moe_experts(a1q, a1s, w, spec.top_k, al, BM, spec.activation, sh_in, sh_s,
+                               workspace=ws)
     torch.cuda.synchronize()
     hw = _host_w(d)
     refs = {}
     for mode in ("exact", "mirrored"):
         refs[mode] = oracle.experts(ra, rs, rid, hw["w13"], hw.get("w13_scale"), hw["w2"],
                                     hw.get("w2_scale"), spec.activation, mode, shared)
-    path = "fp8" if spec.quant == "fp8" else "bf16"
+    fp8 = spec.quant == "fp8"
+    path = "fp8" if fp8 else "bf16"
     check_tolerance(f64_of_bf16(feo), f64_of_bf16(refs["exact"][0]), f64_of_bf16(refs["mirrored"][0]),
-                    path, f"{spec.name} fused_expert_output")
+                    path, f"{spec.name} fused_expert_output", elementwise=not fp8)
     if spec.shared_I:
         check_tolerance(f64_of_bf16(sho), f64_of_bf16(refs["exact"][1]),
-                        f64_of_bf16(refs["mirrored"][1]), path, f"{spec.name} shared_out")
+                        f64_of_bf16(refs["mirrored"][1]), path, f"{spec.name} shared_out",
+                        elementwise=not fp8)
+    if fp8:
+        _check_fp8_stages(moe, spec, w, BM, ws, al, rid, ra, rs, hw, shared, feo, sho)
+
+
+def _check_fp8_stages(moe, spec, w, BM, ws, al, rid, ra, rs, hw, shared, feo, sho):
+    """fp8 path, stage by stage: (1) the GPU's intermediate z codes and scales
+    against the oracle's quantisation of its own z; (2) GEMM-2 against the
+    oracle's GEMM-2 applied to the very z the GPU consumed, per element."""
+    lay = moe.moe_experts_workspace_layout(spec.T, spec.H, spec.top_k, w, spec.activation, BM)
+    I, Is, H, k = spec.I, spec.shared_I, spec.H, spec.top_k
+    raw = ws.cpu().numpy()
+    rows = lay["rows"]
+    zq = raw[lay["z"]:lay["z"] + rows * I].reshape(rows, I)
+    zs = raw[lay["z_scale"]:lay["z_scale"] + rows * (I // 128) * 4].view(np.float32).reshape(rows, I // 128)
+    sorted_ids = al["sorted_token_ids"].cpu().numpy()
+    ntp = int(al["num_tokens_post_padded"].cpu().numpy()[0])
+    A = oracle.moe.dequant_act(ra, rs)
+    got_y, ref_y, same = [], [], []
+    for e in np.unique(rid):
+        r_idx = np.array([r for r in range(ntp) if sorted_ids[r] < spec.T * k
+                          and rid.reshape(-1)[sorted_ids[r]] == e])
+        flat = sorted_ids[r_idx]
+        W13 = oracle.moe.dequant_weight(hw["w13"][e], hw["w13_scale"][e])
+        W2 = oracle.moe.dequant_weight(hw["w2"][e], hw["w2_scale"][e])
+        z_ref = oracle.moe.expert_gemm1(A[flat // k], W13, spec.activation)
+        same.append(check_fp8_codes(zq[r_idx], zs[r_idx], z_ref, f"{spec.name} expert {e} z"))
+        y = oracle.moe.expert_gemm2(oracle.dequant_g128(zq[r_idx], zs[r_idx]), W2)
+        ref_y.append(f64_of_bf16(oracle.f64_to_bf16_bits(y)))
+        got_y.append(f64_of_bf16(feo).reshape(spec.T * k, H)[flat])
+    g, r = np.concatenate(got_y), np.concatenate(ref_y)
+    check_tolerance(g, r, r, "bf16", f"{spec.name} GEMM-2 given the GPU's z")
+    assert np.mean(same) > 0.995
+    if spec.shared_I:
+        zq = raw[lay["shared_z"]:lay["shared_z"] + spec.T * Is].reshape(spec.T, Is)
+        zs = raw[lay["shared_z_scale"]:lay["shared_z_scale"] + spec.T * (Is // 128) * 4] \
+            .view(np.float32).reshape(spec.T, Is // 128)
+        W13 = oracle.moe.dequant_weight(shared["w13"], shared["w13_scale"])
+        W2 = oracle.moe.dequant_weight(shared["w2"], shared["w2_scale"])
+        z_ref = oracle.moe.expert_gemm1(oracle.moe.dequant_act(shared["a"], shared["a_scale"]), W13,
+                                        spec.activation)
+        assert check_fp8_codes(zq, zs, z_ref, f"{spec.name} shared z") > 0.995
+        y = f64_of_bf16(oracle.f64_to_bf16_bits(
+            oracle.moe.expert_gemm2(oracle.dequant_g128(zq, zs), W2)))
+        check_tolerance(f64_of_bf16(sho), y, y, "bf16", f"{spec.name} shared GEMM-2 given the GPU's z")
 
 
 # ------------------------------------------------------- whole layer, reduced
@@ -121,7 +171,8 @@ def test_forward_reduced(spec):
                                         spec.eps, spec.out_quant)
         torch.cuda.synchronize()
         check_tolerance(_out_f64(spec, out, scale), _ref_f64(spec, refs["exact"]),
-                        _ref_f64(spec, refs["mirrored"]), _path(spec), f"{spec.name} BM={bm}")
+                        _ref_f64(spec, refs["mirrored"]), _path(spec), f"{spec.name} BM={bm}",
+                        elementwise=spec.quant != "fp8")
 
 
 def test_forward_zero_tokens_is_a_no_op():
@@ -224,4 +275,4 @@ def test_forward_full_size_sampled(spec):
             for mode in ("exact", "mirrored")}
     got = _out_f64(spec, out, scale, sample)
     check_tolerance(got, _ref_f64(spec, refs["exact"]), _ref_f64(spec, refs["mirrored"]),
-                    _path(spec), spec.name)
+                    _path(spec), spec.name, elementwise=spec.quant != "fp8")

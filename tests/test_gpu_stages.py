@@ -203,10 +203,11 @@ def _finalize_case(spec, sample=None):
         got = f64_of_bf16(to_numpy_bits(out)[sel])
         ref = f64_of_bf16(ro)
         check_tolerance(got, ref, ref, "bf16", spec.name)
-    # residual_out = bf16(acc): at most one bf16 ulp apart (fp32 vs fp64 accumulation)
+    # residual_out = bf16(acc): one bf16 ulp apart at most, plus the fp32-vs-fp64
+    # accumulation error where the sum cancels towards zero
     gr = f64_of_bf16(to_numpy_bits(res_out)[sel])
     rr = f64_of_bf16(rres)
-    assert np.all(np.abs(gr - rr) <= np.abs(rr) * 2.0 ** -7 + 1e-30)
+    assert np.all(np.abs(gr - rr) <= np.abs(rr) * 2.0 ** -7 + 1e-5)
 
 
 @pytest.mark.parametrize("spec", CONFIGS["finalize"], ids=lambda s: s.name)
