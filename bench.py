@@ -35,7 +35,8 @@ def parse():
                     help="family@T<tokens>, e.g. mixtral@T4096, deepseek_v3@T8192, llama4@T2048")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    X
+    ap.add_argument("--cpu-sample", type=int, default=512,
+                    help="tokens in the oracle's timed sample (about 10-30 s of CPU work)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 counters (json)")
     return ap.parse_args()
