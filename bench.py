@@ -109,7 +109,7 @@ def main():
     d = make_layer_inputs(spec, device=dev)
     w = moe.make_weights(*(d.get(k) for k in ("w13", "w2", "w13_scale", "w2_scale", "shared_w13",
                                               "shared_w2", "shared_w13_scale", "shared_w2_scale")))
-    bm = a.block_m or moe.moe_pick_block_m(spec.T, spec.top_k, spec.E)
+    bm = a.block_m or moe.moe_pick_block_m(spec.T, spec.top_k, spec.E, spec.quant)
     stream = torch.cuda.current_stream()
 
     def step(events=None, ws=None, out=None):

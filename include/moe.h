@@ -252,8 +252,10 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
 size_t moe_forward_workspace_bytes(int T, int H, int top_k, const moe_weights* weights,
                                    int activation, int block_m,
                                    int apply_router_weight_on_input);
-/* (host) the block_m moe_forward uses when given 0. */
-int moe_pick_block_m(int T, int top_k, int num_experts);
+/* (host) the block_m moe_forward uses when given 0, by the average rows per
+ * expert a = T*top_k/E: 16 (a <= 16), 32 (a <= 32), then bf16: 64 (a <= 64)
+ * else 256; fp8: 64 (a <= 96) else 128.  quant is a moe_quant. */
+int moe_pick_block_m(int T, int top_k, int num_experts, int quant);
 
 #ifdef __cplusplus
 }

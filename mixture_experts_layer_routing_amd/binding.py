@@ -52,7 +52,7 @@ def _load():
     sig = {
         "moe_status_str": (ctypes.c_char_p, [c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
-        "moe_pick_block_m": (c_int, [c_int, c_int, c_int]),
+        "moe_pick_block_m": (c_int, [c_int, c_int, c_int, c_int]),
         "moe_route": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
         "moe_prepare": (c_int, [c_vp, c_int, c_int, c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
         "moe_align": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -131,8 +131,8 @@ def make_weights(w13, w2, w13_scale=None, w2_scale=None, shared_w13=None, shared
     return w
 
 
-def moe_pick_block_m(T, top_k, num_experts):
-    return _lib.moe_pick_block_m(T, top_k, num_experts)
+def moe_pick_block_m(T, top_k, num_experts, quant="none"):
+    return _lib.moe_pick_block_m(T, top_k, num_experts, QUANT[quant])
 
 
 def moe_align_capacity(T, top_k, E, block_m):

@@ -64,6 +64,13 @@ def build(jobs=None, verbose=False):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{r.stderr}")
+    # A kernel whose host-side stub was dropped (e.g. a device-only builtin in
+    # a kernel body) links fine but fails at dlopen: refuse such a library.
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    r = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("undefined kernel stubs in libmoe.so:\n" + "\n".join(missing[:5]))
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,7 +1,9 @@
 // align: sort the flat rows i = t*top_k + j by expert into block_m-padded
 // groups, deterministically (ascending i inside every expert).
 //
-// The ids are cut into tiles of 4096.  count: one workgroup per tile builds
+// The ids are cut into tiles of 1024 (four 256-id steps per workgroup: the
+// ballot grouping costs one pass per distinct id in a wave, so short tiles
+// spread it over many workgroups).  count: one workgroup per tile builds
 // the tile's expert histogram with LDS atomics (order-free).  scan: one
 // workgroup turns the [tile][expert] counts into per-expert totals, padded
 // offsets (exclusive scan), per-(tile, expert) write bases, block owners and
@@ -10,14 +12,14 @@
 // (stable rank = lanes below with the same id), waves of the same step are
 // ordered through a small LDS table, and a per-expert LDS cursor carries the
 // position across steps.  No global atomics, so the result is bit-exact.
-// A single-tile input (T*k <= 4096) runs all three phases in one launch.
+// A single-tile input (T*k <= 1024) runs all three phases in one launch.
 #include "moe_device.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTile = 4096;
+constexpr int kTile = 1024;
 constexpr int kMaxE = 1024;
 
 // Exclusive scan of v[0..count) in LDS by all NT threads of the block;

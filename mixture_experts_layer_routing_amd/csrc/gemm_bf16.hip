@@ -1,50 +1,84 @@
 // bf16 grouped-GEMM instantiations (see gemm_impl.h for the kernel).
 //
-// Tile shapes by align block size BM (rows per expert block):
+// Tile shapes by align block size BM (rows per expert block) and output
+// tile width BNZ (z columns for the gated first GEMM, whose weight tile is
+// 2*BNZ rows):
 //   BM 16/32  -- 16x16x32 MFMA, the 4 waves split N (skinny, weight-streaming)
-//   BM 64/128 -- 32x32x16 MFMA, 2x2 waves
-//   BM 256    -- 32x32x16 MFMA, 4x1 waves, 64x64 (gated: x2) per wave
-// Gated first GEMM: 64 z columns per tile (64 gate + 64 up weight rows);
-// everything else 128 output columns per tile.
+//   BM 64     -- 32x32x16 MFMA, 2x2 waves of 32 x BNZ/2
+//   BM 128    -- 32x32x16 MFMA, 2x4 waves of 64 x BNZ/4 (BNZ 64: 2x2 waves)
+//   BM 256    -- 32x32x16 MFMA, 2x4 waves (two per SIMD) of 128 x BNZ/4
+//                (gated: x2), 128 fp32 accumulators per lane
 #include "gemm_impl.h"
 
 namespace moe {
 
-template <int AM, int EP, bool GATED, int BNZ>
-static void dispatch_bm(int block_m, const GemmParams& p, int64_t max_mblk, hipStream_t s) {
-  switch (block_m) {
-    case 16: launch_gemm<GemmCfg<16, BNZ, 1, 4, 16, false, GATED, AM, EP>>(p, max_mblk, s); break;
-    case 32: launch_gemm<GemmCfg<32, BNZ, 1, 4, 16, false, GATED, AM, EP>>(p, max_mblk, s); break;
-    case 64: launch_gemm<GemmCfg<64, BNZ, 2, 2, 32, false, GATED, AM, EP>>(p, max_mblk, s); break;
-    case 128: launch_gemm<GemmCfg<128, BNZ, 2, 2, 32, false, GATED, AM, EP>>(p, max_mblk, s); break;
-    default: launch_gemm<GemmCfg<256, BNZ, 4, 1, 32, false, GATED, AM, EP>>(p, max_mblk, s); break;
+// LDS stages per tile.  Measured on MI355X (Mixtral-shaped GEMMs): a third
+// or fourth stage costs more in occupancy (fewer resident workgroups) than
+// it gains in latency hiding at every tile size tried, so two it is.
+constexpr int bf16_stages(int bm, int nb) {
+  (void)bm;
+  (void)nb;
+  return 2;
+}
+
+// Wave grid of the 256-row tiles: 8 waves (2 per SIMD), each 128 rows x a
+// quarter of the tile's columns; two waves per SIMD let one issue MFMAs
+// while the other waits on LDS or the barrier.  Same for 128 x 128 tiles.
+constexpr int kW256M = 2, kW256N = 4;
+constexpr int kW128M = 2, kW128N = 4;
+
+template <int BM, int BNZ, int WM, int WN, int MF, bool GATED, int AM, int EP>
+using Bf16Cfg = GemmCfg<BM, BNZ, WM, WN, MF, false, GATED, AM, EP,
+                        bf16_stages(BM, GATED ? 2 * BNZ : BNZ)>;
+
+template <int AM, int EP, bool GATED>
+static void dispatch_bm(int block_m, int bnz, const GemmParams& p, int64_t max_mblk,
+                        hipStream_t s) {
+  if (block_m == 16) {
+    if (bnz == 64) launch_gemm<Bf16Cfg<16, 64, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
+    else launch_gemm<Bf16Cfg<16, 128, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
+  } else if (block_m == 32) {
+    if (bnz == 64) launch_gemm<Bf16Cfg<32, 64, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
+    else launch_gemm<Bf16Cfg<32, 128, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
+  } else if (block_m == 64) {
+    if (bnz == 64) launch_gemm<Bf16Cfg<64, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
+    else launch_gemm<Bf16Cfg<64, 128, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
+  } else if (block_m == 128) {
+    if (bnz == 64) launch_gemm<Bf16Cfg<128, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
+    else launch_gemm<Bf16Cfg<128, 128, kW128M, kW128N, 32, GATED, AM, EP>>(p, max_mblk, s);
+  } else {
+    if (bnz == 64) launch_gemm<Bf16Cfg<256, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
+    else if (bnz == 128) launch_gemm<Bf16Cfg<256, 128, kW256M, kW256N, 32, GATED, AM, EP>>(p, max_mblk, s);
+    else launch_gemm<Bf16Cfg<256, 256, kW256M, kW256N, 32, false, AM, EP>>(p, max_mblk, s);
   }
 }
 
-void launch_gemm_bf16(int kind, bool gated, int block_m, const GemmParams& p, int64_t max_mblk,
-                      hipStream_t s) {
+void launch_gemm_bf16(int kind, bool gated, int block_m, int bnz, const GemmParams& p,
+                      int64_t max_mblk, hipStream_t s) {
   switch (kind) {
     case GEMM_Z_ROUTED:
-      if (gated) dispatch_bm<A_GATHER, EPI_Z, true, 64>(block_m, p, max_mblk, s);
-      else dispatch_bm<A_GATHER, EPI_Z, false, 128>(block_m, p, max_mblk, s);
+      if (gated) dispatch_bm<A_GATHER, EPI_Z, true>(block_m, bnz, p, max_mblk, s);
+      else dispatch_bm<A_GATHER, EPI_Z, false>(block_m, bnz, p, max_mblk, s);
       break;
     case GEMM_Y_ROUTED:
-      dispatch_bm<A_ROWS, EPI_OUT_ROUTED, false, 128>(block_m, p, max_mblk, s);
+      dispatch_bm<A_ROWS, EPI_OUT_ROUTED, false>(block_m, bnz, p, max_mblk, s);
       break;
     case GEMM_Z_DENSE:
-      if (gated) dispatch_bm<A_DENSE, EPI_Z, true, 64>(block_m, p, max_mblk, s);
-      else dispatch_bm<A_DENSE, EPI_Z, false, 128>(block_m, p, max_mblk, s);
+      if (gated) dispatch_bm<A_DENSE, EPI_Z, true>(block_m, bnz, p, max_mblk, s);
+      else dispatch_bm<A_DENSE, EPI_Z, false>(block_m, bnz, p, max_mblk, s);
       break;
     default:
-      dispatch_bm<A_DENSE, EPI_OUT_DENSE, false, 128>(block_m, p, max_mblk, s);
+      dispatch_bm<A_DENSE, EPI_OUT_DENSE, false>(block_m, bnz, p, max_mblk, s);
       break;
   }
 }
 
-int gemm_tile_n(int kind, bool fp8, bool gated, int block_m) {
-  (void)block_m;
-  if (!fp8 && gated && (kind == GEMM_Z_ROUTED || kind == GEMM_Z_DENSE)) return 64;
-  return 128;
+int gemm_tile_n(int kind, bool fp8, bool gated, int block_m, int n) {
+  if (fp8) return 128;
+  const bool first = kind == GEMM_Z_ROUTED || kind == GEMM_Z_DENSE;
+  if (first && gated) return (block_m >= 128 && n % 128 == 0) ? 128 : 64;
+  if (first) return 128;
+  return (block_m == 256 && n % 256 == 0) ? 256 : 128;
 }
 
 }  // namespace moe

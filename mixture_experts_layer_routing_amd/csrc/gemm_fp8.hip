@@ -3,7 +3,8 @@
 // Every tile is 128 output columns wide: on the first GEMM that is one
 // 128-column group of z, so the fused re-quantisation of z to E4M3 G(128)
 // finds each group's amax inside the tile.  BM 16/32 use 16x16x128 MFMA with
-// the waves split along N, BM 64/128 use 32x32x64 MFMA on 2x2 waves.
+// 4 waves split along N, BM 64/128 use 32x32x64 MFMA on 2x4 waves (two per
+// SIMD).
 #include "gemm_impl.h"
 
 namespace moe {
@@ -13,13 +14,14 @@ static void dispatch_bm(int block_m, const GemmParams& p, int64_t max_mblk, hipS
   switch (block_m) {
     case 16: launch_gemm<GemmCfg<16, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s); break;
     case 32: launch_gemm<GemmCfg<32, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s); break;
-    case 64: launch_gemm<GemmCfg<64, 128, 2, 2, 32, true, GATED, AM, EP>>(p, max_mblk, s); break;
-    default: launch_gemm<GemmCfg<128, 128, 2, 2, 32, true, GATED, AM, EP>>(p, max_mblk, s); break;
+    case 64: launch_gemm<GemmCfg<64, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s); break;
+    default: launch_gemm<GemmCfg<128, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s); break;
   }
 }
 
-void launch_gemm_fp8(int kind, bool gated, int block_m, const GemmParams& p, int64_t max_mblk,
-                     hipStream_t s) {
+void launch_gemm_fp8(int kind, bool gated, int block_m, int bnz, const GemmParams& p,
+                     int64_t max_mblk, hipStream_t s) {
+  (void)bnz;  // always 128
   switch (kind) {
     case GEMM_Z_ROUTED:
       if (gated) dispatch_bm<A_GATHER, EPI_Z, true>(block_m, p, max_mblk, s);

@@ -7,14 +7,17 @@
 // block-padded row groups come from align; the shared expert runs the same
 // kernel in "dense" mode over all T rows.
 //
-// Tiling: 256 threads = 4 waves, tile BM x NB (NB = 2*BNZ when gated: BNZ
+// Tiling: 4 or 8 waves, tile BM x NB (NB = 2*BNZ when gated: BNZ
 // gate rows n0.. and the matching BNZ up rows I+n0.., so SiLU-mul is
 // elementwise in registers).  Each k-tile is 128 bytes of K per row (64 bf16
-// or 128 fp8 elements), staged global -> registers -> LDS, double-buffered
-// with one barrier per k-tile; the next tile's global loads are in flight
+// or 128 fp8 elements), moved global -> LDS by direct-to-LDS loads
+// (global_load_lds_dwordx4: no staging registers, no ds_write), double-
+// buffered with one barrier per k-tile; the next tile's loads are in flight
 // while the current one feeds the MFMAs.  LDS rows are 128 B with the 16-byte
-// chunk index XOR-swizzled by (row & 7), so the fragment reads (8 lanes = 8
-// rows at one chunk column) hit all 32 banks.
+// chunk index XOR-swizzled by (row >> 1) & 7, so the fragment reads (16
+// lanes = 16 rows at one chunk column) hit all 64 banks; a direct load writes 64 lanes x
+// 16 B contiguously, so each lane fetches the global chunk that belongs in
+// its slot.  Fragments whose rows are all padding skip their MFMAs.
 //
 // MFMA: bf16 v_mfma_f32_32x32x16_bf16 / 16x16x32_bf16; fp8 E4M3
 // v_mfma_f32_32x32x64_f8f6f4 / 16x16x128_f8f6f4.  Operand lane layout: lane l
@@ -33,6 +36,8 @@
 // and weight tiles through that XCD's L2.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_device.h"
 #include "launch.h"
 
@@ -42,15 +47,29 @@ enum { A_GATHER = 0, A_ROWS = 1, A_DENSE = 2 };
 enum { EPI_Z = 0, EPI_OUT_ROUTED = 1, EPI_OUT_DENSE = 2 };
 
 template <int BM_, int BNZ_, int WAVES_M_, int WAVES_N_, int MF_, bool FP8_, bool GATED_,
-          int AMODE_, int EPI_>
+          int AMODE_, int EPI_, int NSTAGE_ = 2, int PF_ = -1>
 struct GemmCfg {
   static constexpr int BM = BM_, BNZ = BNZ_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, MF = MF_;
   static constexpr bool FP8 = FP8_, GATED = GATED_;
   static constexpr int AMODE = AMODE_, EPI = EPI_;
+  // LDS stages: NSTAGE-1 k-tiles of direct-to-LDS loads in flight while
+  // one is consumed (one barrier per k-tile either way).
+  static constexpr int NSTAGE = NSTAGE_;
+  // L2 prefetch distance in k-tiles (0 = off, -1 = the library default).
+  static constexpr int PF = PF_;
 };
 
+// Default L2 prefetch distance (k-tiles ahead of the one being consumed).
+constexpr int kDefaultPrefetch = 0;
+
+// gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16 lanes per
+// cycle (256 B).  Rows are 128 B, so rows r and r+2 share banks; XOR-ing the
+// chunk with (row >> 1) & 7 gives the 8 rows of each parity among 16
+// consecutive rows 8 distinct chunks, so a fragment read (16 lanes = 16
+// consecutive rows at one chunk column) touches all 64 banks once.
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+  return row * 128 + ((chunk ^ swz_key(row)) << 4);
 }
 
 template <int MF, bool FP8>
@@ -136,30 +155,68 @@ __device__ __forceinline__ int acc_col(int lane) {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// 64 lanes x 16 bytes from per-lane global addresses into 1 KB of LDS,
+// lane i landing at lds + 16*i (global_load_lds_dwordx4).
+__device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* lds) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
+// L2 prefetch: one 4-byte direct-to-LDS load per lane into a 256-byte sink
+// (contents discarded) pulls each lane's 128-byte line into the caches
+// without tying up a VGPR.
+__device__ __forceinline__ void l2_prefetch_line(const uint8_t* g, uint8_t* sink) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)sink, 4, 0, 0);
+}
+
+// Wait for every outstanding global (and direct-to-LDS) load of this wave.
+__device__ __forceinline__ void wait_vm_loads() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Wait until at most N of this wave's global loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm_loads_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <class C>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_kernel(GemmParams p) {
   constexpr int BM = C::BM, BNZ = C::BNZ, MF = C::MF;
   constexpr bool FP8 = C::FP8;
   constexpr int G = C::GATED ? 2 : 1;
   constexpr int NB = G * BNZ;
   constexpr int WM = BM / C::WAVES_M, WN = BNZ / C::WAVES_N;
   constexpr int FM = WM / MF, FN = WN / MF;
-  static_assert(C::WAVES_M * C::WAVES_N == 4, "4 waves");
+  constexpr int NW = C::WAVES_M * C::WAVES_N;   // waves per workgroup
+  constexpr int NT = 64 * NW;                     // threads per workgroup
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(FM >= 1 && FN >= 1 && WM % MF == 0 && WN % MF == 0, "wave tile");
   constexpr int A_BYTES = BM * 128, B_BYTES = NB * 128, STAGE = A_BYTES + B_BYTES;
-  constexpr int A_CH = (BM * 8 + 255) / 256;
-  constexpr int B_CH = NB * 8 / 256;
-  static_assert(NB * 8 % 256 == 0, "B tile");
+  constexpr int ROWS = BM + NB;           // LDS rows per stage: A rows, then B rows
+  static_assert(ROWS % 8 == 0, "8-row load groups");
+  constexpr int NI = ROWS / 8;            // 1 KB direct-to-LDS loads per k-tile
+  constexpr int NIW = (NI + NW - 1) / NW; // ... per wave (at most)
   constexpr int EB = FP8 ? 1 : 2;
   typedef Mfma<MF, FP8> M;
   typedef typename M::acc_t acc_t;
   typedef typename M::frag_t frag_t;
   constexpr int NSUB = M::NSUB, NACC = M::NACC;
-  constexpr int SA_BYTES = FP8 ? 2 * BM * 4 : 0;
   constexpr int EPI_BYTES = (C::EPI == EPI_Z && FP8) ? BM * BNZ * 4 : BM * BNZ * 2;
-  constexpr int SMEM = cmax(2 * STAGE + SA_BYTES, EPI_BYTES);
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-  float* sA = reinterpret_cast<float*>(smem + 2 * STAGE);
+  constexpr int NSTAGE = C::NSTAGE;
+  constexpr int PF = C::PF < 0 ? kDefaultPrefetch : C::PF;
+  static_assert(PF == 0 || NSTAGE == 2, "L2 prefetch runs with two LDS stages");
+  constexpr int PFI = PF > 0 ? (ROWS / 64 + NW - 1) / NW : 0;  // prefetch loads per wave per k-tile
+  static_assert(NSTAGE == 2 || (!FP8 && NI % NW == 0), "deeper pipelines: bf16, whole load groups");
+  constexpr int SMEM = cmax(NSTAGE * STAGE, EPI_BYTES);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+  __shared__ float sA[FP8 ? 2 * BM : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t pf_sink[256];
+  // fp8: the tile's weight-block scales along K (gate row, then up row)
+  constexpr int kMaxKB = 128;  // K <= 16384
+  __shared__ float sW[FP8 ? 2 * kMaxKB : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -185,87 +242,125 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
   const uint8_t* wbase = p.w;
   const float* wsbase = p.w_scale;
   if constexpr (C::AMODE != A_DENSE) {
-    const int e = p.block_expert[mblk];
+    // the tile may be a fraction of the align block (GEMM-2 at BM/2)
+    const int e = p.block_expert[m0 / p.align_bm];
     wbase += static_cast<int64_t>(e) * p.w_stride;
     if constexpr (FP8) wsbase += static_cast<int64_t>(e) * p.ws_stride;
   }
   const int nflat = p.T * p.top_k;
-  const int kc = tid & 7;
   const int64_t krow_bytes = static_cast<int64_t>(p.K) * EB;
   const int kblocks = p.K / 128;  // fp8: scale blocks along K (= k-tiles)
 
-  // ---- A rows for this thread's chunks ----
-  const uint8_t* a_ptr[A_CH];
-  bool a_ok[A_CH];
-  int a_src[A_CH];
+  // Rows of this block that carry data: pad rows sit at the end of an
+  // expert's segment (and past T in dense mode), so a count is enough.
+  int valid_rows;
+  if constexpr (C::AMODE == A_DENSE) {
+    valid_rows = min(BM, p.T - m0);
+  } else {
+    int v = 0;
+    for (int r = tid; r < BM; r += NT) v += p.sorted[m0 + r] < nflat ? 1 : 0;
+    valid_rows = __syncthreads_count(v);
+    if (valid_rows == 0) return;  // a tile past its expert's rows (block-uniform)
+  }
+
+  // ---- direct-to-LDS source pointers ----
+  // Load group j covers LDS rows 8j..8j+7 of a stage; lane i fills the
+  // 16-byte slot i of the group, i.e. row 8j + i/8 at physical chunk i%8,
+  // which holds logical chunk (i%8) ^ swz_key(row).
+  const uint8_t* src[NIW];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + 256 * i;
-    const int row = c >> 3;
-    const bool in = c < BM * 8;
-    int src = 0;
-    bool ok = false;
-    if (in) {
-      if constexpr (C::AMODE == A_GATHER) {
-        const int sid = p.sorted[m0 + row];
-        ok = sid < nflat;
-        src = ok ? sid / p.top_k : 0;
-      } else if constexpr (C::AMODE == A_ROWS) {
-        ok = true;
-        src = m0 + row;
+  for (int s = 0; s < NIW; ++s) {
+    const int j = wave + NW * s;
+    const int r = 8 * j + (lane >> 3);
+    const int lchunk = (lane & 7) ^ swz_key(r);
+    const uint8_t* ptr = p.a;  // any valid row; unused when j >= NI
+    if (j < NI) {
+      if (r < BM) {
+        int srow = 0;
+        if constexpr (C::AMODE == A_GATHER) {
+          const int sid = p.sorted[m0 + r];
+          srow = sid < nflat ? sid / p.top_k : 0;   // pad rows read token 0 (discarded)
+        } else if constexpr (C::AMODE == A_ROWS) {
+          srow = m0 + r;
+        } else {
+          srow = min(m0 + r, p.T - 1);
+        }
+        ptr = p.a + static_cast<int64_t>(srow) * krow_bytes;
       } else {
-        ok = m0 + row < p.T;
-        src = ok ? m0 + row : 0;
+        const int b = r - BM;
+        int wrow;
+        if constexpr (C::GATED) wrow = b < BNZ ? n0 + b : p.inter + n0 + (b - BNZ);
+        else wrow = n0 + b;
+        ptr = wbase + static_cast<int64_t>(wrow) * krow_bytes;
       }
     }
-    a_ok[i] = ok;
-    a_src[i] = src;
-    a_ptr[i] = p.a + static_cast<int64_t>(src) * krow_bytes + kc * 16;
+    src[s] = ptr + lchunk * 16;
   }
-  const uint8_t* b_ptr[B_CH];
+  // L2 prefetch rows: load u of this wave covers tile rows 64*(wave + NW*u)
+  // + lane (A rows, then B rows; past the end it repeats row 0).
+  const uint8_t* pf_src[PFI > 0 ? PFI : 1];
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int brow = (tid + 256 * i) >> 3;
-    int wrow;
-    if constexpr (C::GATED) wrow = brow < BNZ ? n0 + brow : p.inter + n0 + (brow - BNZ);
-    else wrow = n0 + brow;
-    b_ptr[i] = wbase + static_cast<int64_t>(wrow) * krow_bytes + kc * 16;
+  for (int u = 0; u < PFI; ++u) {
+    const int r = 64 * (wave + NW * u) + lane;
+    const uint8_t* ptr = p.a;
+    if (r < BM) {
+      int srow = 0;
+      if constexpr (C::AMODE == A_GATHER) {
+        const int sid = p.sorted[m0 + r];
+        srow = sid < nflat ? sid / p.top_k : 0;
+      } else if constexpr (C::AMODE == A_ROWS) {
+        srow = m0 + r;
+      } else {
+        srow = min(m0 + r, p.T - 1);
+      }
+      ptr = p.a + static_cast<int64_t>(srow) * krow_bytes;
+    } else if (r < ROWS) {
+      const int b = r - BM;
+      int wrow;
+      if constexpr (C::GATED) wrow = b < BNZ ? n0 + b : p.inter + n0 + (b - BNZ);
+      else wrow = n0 + b;
+      ptr = wbase + static_cast<int64_t>(wrow) * krow_bytes;
+    }
+    pf_src[u] = ptr;
   }
-  // fp8 weight-scale rows (gate block, up block) for this N-tile
+  // fp8: this thread's activation-scale row (threads < BM) and the weight-scale rows
+  static_assert(!FP8 || BM <= NT, "one activation-scale row per thread");
+  int a_srow = 0;
   const float* sw_row0 = nullptr;
   const float* sw_row1 = nullptr;
   if constexpr (FP8) {
-    sw_row0 = wsbase + static_cast<int64_t>(n0 / 128) * kblocks;
-    if constexpr (C::GATED) sw_row1 = wsbase + static_cast<int64_t>((p.inter + n0) / 128) * kblocks;
-  }
-
-  u32x4 ra[A_CH], rb[B_CH];
-  float rsa[A_CH];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      if (a_ok[i]) ra[i] = *reinterpret_cast<const u32x4*>(a_ptr[i] + kt * 128);
-      else ra[i] = u32x4{0u, 0u, 0u, 0u};
-      if constexpr (FP8)
-        rsa[i] = (a_ok[i] && kc == 0) ? p.a_scale[static_cast<int64_t>(a_src[i]) * kblocks + kt] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_ptr[i] + kt * 128);
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* As = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + 256 * i;
-      if (c < BM * 8) {
-        *reinterpret_cast<u32x4*>(As + swz(c >> 3, kc)) = ra[i];
-        if constexpr (FP8) if (kc == 0) sA[buf * BM + (c >> 3)] = rsa[i];
+    if (tid < BM) {
+      if constexpr (C::AMODE == A_GATHER) {
+        const int sid = p.sorted[m0 + tid];
+        a_srow = sid < nflat ? sid / p.top_k : 0;
+      } else if constexpr (C::AMODE == A_ROWS) {
+        a_srow = m0 + tid;
+      } else {
+        a_srow = min(m0 + tid, p.T - 1);
       }
     }
+    sw_row0 = wsbase + static_cast<int64_t>(n0 / 128) * kblocks;
+    if constexpr (C::GATED) sw_row1 = wsbase + static_cast<int64_t>((p.inter + n0) / 128) * kblocks;
+    for (int i = tid; i < kblocks; i += NT) {
+      sW[i] = sw_row0[i];
+      if constexpr (C::GATED) sW[kMaxKB + i] = sw_row1[i];
+    }
+    // made visible by the first k-tile's barrier
+  }
+
+  auto prefetch = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      *reinterpret_cast<u32x4*>(As + A_BYTES + swz((tid + 256 * i) >> 3, kc)) = rb[i];
+    for (int u = 0; u < PFI; ++u) l2_prefetch_line(pf_src[u] + static_cast<int64_t>(kt) * 128, pf_sink);
   };
+  auto dma = [&](int kt, int buf) {
+#pragma unroll
+    for (int s = 0; s < NIW; ++s) {
+      const int j = wave + NW * s;
+      if (NI % NW == 0 || j < NI)
+        lds_dma16(src[s] + static_cast<int64_t>(kt) * 128, smem + buf * STAGE + j * 1024);
+    }
+  };
+
 
   acc_t acc[G][FM][FN];
 #pragma unroll
@@ -278,61 +373,144 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
         for (int v = 0; v < NACC; ++v) acc[g][fm][fn][v] = 0.f;
 
   const int nk = p.K / (128 / EB);
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* As = smem + buf * STAGE;
-    const uint8_t* Bs = As + A_BYTES;
-    frag_t fa[NSUB][FM], fb[NSUB][G][FN];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        fa[s][fm] = M::read(As, wm * WM + fm * MF + (lane & (MF - 1)), s, lane);
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          fb[s][g][fn] = M::read(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+  const int row_w = wm * WM;
+  // fragments of this wave that hold at least one data row (wave-uniform)
+  const int fm_live = __builtin_amdgcn_readfirstlane(
+      valid_rows > row_w ? min(FM, (valid_rows - row_w + MF - 1) / MF) : 0);
+
+  // The k-loop, instantiated twice: branch-free when every fragment row
+  // block holds data (all but an expert's last block), and with uniform
+  // per-fragment guards otherwise.
+  auto kloop = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    float rsa = 0.f;
+    if constexpr (FP8) {
+      if (tid < BM) sA[tid] = p.a_scale[static_cast<int64_t>(a_srow) * kblocks];
     }
-    if constexpr (!FP8) {
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-        for (int g = 0; g < G; ++g)
+    for (int st = 0; st < NSTAGE - 1; ++st)
+      if (st < nk) dma(st, st);
+    int buf = 0;                       // kt % NSTAGE
+    int nbuf = NSTAGE - 1;             // (kt + NSTAGE - 1) % NSTAGE
+    for (int kt = 0; kt < nk; ++kt) {
+      // k-tile kt has landed once at most the loads of the NSTAGE-2 later
+      // k-tiles (NIW per wave each) are still outstanding.
+      if constexpr (NSTAGE > 2) {
+        if (kt + NSTAGE - 2 < nk) wait_vm_loads_but<NIW * (NSTAGE - 2)>();
+        else wait_vm_loads();
+      } else if constexpr (PF > 0) {
+        // the prefetch issued after this k-tile's DMA may stay in flight
+        if (kt >= 1 && kt - 1 + PF < nk) wait_vm_loads_but<PFI>();
+        else wait_vm_loads();
+      } else {
+        wait_vm_loads();
+      }
+      __syncthreads();
+      if (kt + NSTAGE - 1 < nk) {
+        if constexpr (FP8)
+          if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kt + 1];
+        dma(kt + NSTAGE - 1, nbuf);
+      }
+      if constexpr (PF > 0)
+        if (kt + PF < nk) prefetch(kt + PF);
+      const uint8_t* As = smem + buf * STAGE;
+      const uint8_t* Bs = As + A_BYTES;
+      if constexpr (!FP8) {
+        // Two fragment sets: substep s+1's LDS reads are in flight while
+        // substep s's MFMAs issue (interleaved by sched_group_barrier).
+        frag_t fa[2][FM], fb[2][G][FN];
+        auto rd = [&](int s, int set) {
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm)
+            if (FULL || fm < fm_live)
+              fa[set][fm] = M::read(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-              acc[g][fm][fn] = M::mma(fa[s][fm], fb[s][g][fn], acc[g][fm][fn]);
-    } else {
-      const float swg[2] = {sw_row0[kt], C::GATED ? sw_row1[kt] : 0.f};
+              fb[set][g][fn] = M::read(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+        };
+        rd(0, 0);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        // activation scales of this lane's accumulator rows
-        float sa[NACC];
+        for (int s = 0; s < NSUB; ++s) {
+          const int cur = s & 1;
+          if (s + 1 < NSUB) rd(s + 1, cur ^ 1);
 #pragma unroll
-        for (int v = 0; v < NACC; ++v) sa[v] = sA[buf * BM + wm * WM + fm * MF + acc_row<MF>(v, lane)];
+          for (int fm = 0; fm < FM; ++fm)
+            if (FULL || fm < fm_live)
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+              for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            acc_t part;
+                for (int fn = 0; fn < FN; ++fn)
+                  acc[g][fm][fn] = M::mma(fa[cur][fm], fb[cur][g][fn], acc[g][fm][fn]);
+          if constexpr (FULL) {
+            if (s + 1 < NSUB) {
+              constexpr int NR = FM + G * FN, NMM = G * FM * FN;
+              constexpr int PER = NMM / NR > 0 ? NMM / NR : 1;
 #pragma unroll
-            for (int v = 0; v < NACC; ++v) part[v] = 0.f;
-#pragma unroll
-            for (int s = 0; s < NSUB; ++s) part = M::mma(fa[s][fm], fb[s][g][fn], part);
-#pragma unroll
-            for (int v = 0; v < NACC; ++v) acc[g][fm][fn][v] += part[v] * (sa[v] * swg[g]);
+              for (int i = 0; i < NR; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+              }
+              __builtin_amdgcn_sched_group_barrier(0x008, NMM - PER * NR > 0 ? NMM - PER * NR : 0, 0);
+            }
           }
+        }
+      } else {
+        const float swg[2] = {sW[kt], C::GATED ? sW[kMaxKB + kt] : 0.f};
+        const float* sAb = sA + (kt & 1) * BM;
+        // Every live fragment's k-tile partial: the NSUB substeps are issued
+        // across all fragments before any promotion, so no MFMA waits on the
+        // previous one's result.
+        acc_t part[G][FM][FN];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          frag_t fa[FM], fb[G][FN];
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+            if (FULL || fm < fm_live) fa[fm] = M::read(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              fb[g][fn] = M::read(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+            if (FULL || fm < fm_live)
+#pragma unroll
+              for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                  if (s == 0) {
+#pragma unroll
+                    for (int v = 0; v < NACC; ++v) part[g][fm][fn][v] = 0.f;
+                  }
+                  part[g][fm][fn] = M::mma(fa[fm], fb[g][fn], part[g][fm][fn]);
+                }
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          if (!(FULL || fm < fm_live)) continue;
+          float sa[NACC];
+#pragma unroll
+          for (int v = 0; v < NACC; ++v) sa[v] = sAb[row_w + fm * MF + acc_row<MF>(v, lane)];
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+              for (int v = 0; v < NACC; ++v)
+                acc[g][fm][fn][v] += part[g][fm][fn][v] * (sa[v] * swg[g]);
+        }
+        if (kt + 1 < nk && tid < BM) sA[(kt + 1 & 1) * BM + tid] = rsa;
       }
+      buf = buf + 1 == NSTAGE ? 0 : buf + 1;
+      nbuf = nbuf + 1 == NSTAGE ? 0 : nbuf + 1;
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
+  };
+  if (fm_live == FM) kloop(std::true_type{});
+  else kloop(std::false_type{});
+  __syncthreads();
 
   // ---- epilogue ----
   if constexpr (C::EPI == EPI_Z) {
@@ -344,21 +522,22 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int v = 0; v < NACC; ++v) {
-          const int r = wm * WM + fm * MF + acc_row<MF>(v, lane);
+          const int r = row_w + fm * MF + acc_row<MF>(v, lane);
           const int cc = wn * WN + fn * MF + acc_col<MF>(lane);
           float z;
-          if constexpr (C::GATED) z = silu(acc[0][fm][fn][v]) * acc[G - 1][fm][fn][v];
-          else z = silu(acc[0][fm][fn][v]);
+          if constexpr (C::GATED) z = silu_fast(acc[0][fm][fn][v]) * acc[G - 1][fm][fn][v];
+          else z = silu_fast(acc[0][fm][fn][v]);
           if constexpr (FP8) reinterpret_cast<float*>(smem)[r * BNZ + cc] = z;
-          else reinterpret_cast<uint16_t*>(smem)[r * BNZ + cc] = static_cast<uint16_t>(f32_to_bf16(z));
+          else reinterpret_cast<uint16_t*>(smem)[r * BNZ + cc] = static_cast<uint16_t>(f32_to_bf16_hw(z));
         }
     __syncthreads();
     if constexpr (FP8) {
       static_assert(BNZ == 128, "fp8 z tile is one 128-column group");
       const int ch = tid & 15;
+      constexpr int RPP = NT / 16;  // rows per pass
 #pragma unroll
-      for (int i = 0; i < (BM + 15) / 16; ++i) {
-        const int r = (tid >> 4) + 16 * i;
+      for (int i = 0; i < (BM + RPP - 1) / RPP; ++i) {
+        const int r = (tid >> 4) + RPP * i;
         if (r < BM) {  // uniform per 16-lane group
           const float* zr = reinterpret_cast<const float*>(smem) + r * BNZ + ch * 8;
           float f[8];
@@ -385,7 +564,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
       }
     } else {
       constexpr int CPR = BNZ / 8;  // 16-byte chunks per tile row
-      for (int c = tid; c < BM * CPR; c += 256) {
+      for (int c = tid; c < BM * CPR; c += NT) {
         const int r = c / CPR, ch = c % CPR;
         const int grow = m0 + r;
         if (C::AMODE == A_DENSE && grow >= p.T) continue;
@@ -403,23 +582,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int v = 0; v < NACC; ++v) {
-          const int r = wm * WM + fm * MF + acc_row<MF>(v, lane);
+          const int r = row_w + fm * MF + acc_row<MF>(v, lane);
           const int cc = wn * WN + fn * MF + acc_col<MF>(lane);
           reinterpret_cast<uint16_t*>(smem)[r * BNZ + cc] =
-              static_cast<uint16_t>(f32_to_bf16(acc[0][fm][fn][v]));
+              static_cast<uint16_t>(f32_to_bf16_hw(acc[0][fm][fn][v]));
         }
     __syncthreads();
     constexpr int CPR = BNZ / 8;
-    for (int c = tid; c < BM * CPR; c += 256) {
+    for (int c = tid; c < BM * CPR; c += NT) {
       const int r = c / CPR, ch = c % CPR;
+      if (r >= valid_rows) continue;
       int orow;
-      if constexpr (C::EPI == EPI_OUT_ROUTED) {
-        orow = p.sorted[m0 + r];
-        if (orow >= nflat) continue;
-      } else {
-        orow = m0 + r;
-        if (orow >= p.T) continue;
-      }
+      if constexpr (C::EPI == EPI_OUT_ROUTED) orow = p.sorted[m0 + r];
+      else orow = m0 + r;
       const u32x4 v = *reinterpret_cast<const u32x4*>(smem + (r * BNZ + ch * 8) * 2);
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + static_cast<int64_t>(orow) * p.ldo +
                                 n0 + ch * 8) = v;
@@ -432,7 +607,7 @@ void launch_gemm(const GemmParams& p, int64_t max_mblk, hipStream_t s) {
   const int64_t tiles = max_mblk * p.n_tiles;
   const int64_t grid = (tiles + 7) / 8 * 8;
   if (grid == 0) return;
-  grouped_gemm_kernel<C><<<static_cast<unsigned>(grid), 256, 0, s>>>(p);
+  grouped_gemm_kernel<C><<<static_cast<unsigned>(grid), 64 * C::WAVES_M * C::WAVES_N, 0, s>>>(p);
 }
 
 }  // namespace moe

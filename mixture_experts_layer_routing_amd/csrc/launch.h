@@ -39,6 +39,7 @@ struct GemmParams {
   const int32_t* block_expert;
   const int32_t* ntp;
   int T, top_k;
+  int align_bm;            // align block size (routed launches); a multiple of the tile BM
   void* out;               // z / fused_expert_output / shared_out
   float* out_scale;        // fp8 z scales [rows][ldo/128]
   int ldo;                 // output row length in elements
@@ -52,12 +53,13 @@ enum GemmKind {
 };
 
 // Output column tile of a launch (BNZ: z columns for the first GEMM, H
-// columns for the second).
-int gemm_tile_n(int kind, bool fp8, bool gated, int block_m);
-// Launch one grouped GEMM; max_mblk bounds the M-blocks (grid sizing).
-void launch_gemm_bf16(int kind, bool gated, int block_m, const GemmParams& p, int64_t max_mblk,
-                      hipStream_t s);
-void launch_gemm_fp8(int kind, bool gated, int block_m, const GemmParams& p, int64_t max_mblk,
-                     hipStream_t s);
+// columns for the second) for an output of n columns.
+int gemm_tile_n(int kind, bool fp8, bool gated, int block_m, int n);
+// Launch one grouped GEMM with output tile bnz; max_mblk bounds the M-blocks
+// (grid sizing).
+void launch_gemm_bf16(int kind, bool gated, int block_m, int bnz, const GemmParams& p,
+                      int64_t max_mblk, hipStream_t s);
+void launch_gemm_fp8(int kind, bool gated, int block_m, int bnz, const GemmParams& p,
+                     int64_t max_mblk, hipStream_t s);
 
 }  // namespace moe

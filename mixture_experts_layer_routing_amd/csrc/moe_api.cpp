@@ -75,6 +75,8 @@ int check_weights(const moe_weights* w, int H, int activation, bool need_ptrs) {
   if (activation != MOE_ACT_SILU_MUL && activation != MOE_ACT_SILU_NO_MUL)
     return fail(MOE_ERR_UNSUPPORTED, "activation %d not supported", activation);
   if (H <= 0 || H % 128) return fail(MOE_ERR_UNSUPPORTED, "H=%d must be a positive multiple of 128", H);
+  if (H > 16384 || w->inter > 16384 || w->shared_inter > 16384)
+    return fail(MOE_ERR_UNSUPPORTED, "H and I are limited to 16384 (fp8 scale staging, K > 16384)");
   const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
   const bool gated = activation == MOE_ACT_SILU_MUL;
   const int step = (!fp8 && gated) ? 64 : 128;
@@ -151,9 +153,9 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   float *zs, *zshs;
   experts_ws(T, top_k, w, bm, c, &z, &zs, &zsh, &zshs);
   const Caps cp = capacities(T, top_k, E, bm);
-  auto launch = [&](int kind, int blk_m, const GemmParams& p, int64_t max_mblk) {
-    if (fp8) launch_gemm_fp8(kind, gated, blk_m, p, max_mblk, s);
-    else launch_gemm_bf16(kind, gated, blk_m, p, max_mblk, s);
+  auto launch = [&](int kind, int blk_m, int bnz, const GemmParams& p, int64_t max_mblk) {
+    if (fp8) launch_gemm_fp8(kind, gated, blk_m, bnz, p, max_mblk, s);
+    else launch_gemm_bf16(kind, gated, blk_m, bnz, p, max_mblk, s);
   };
   // routed first GEMM: gather a1q rows, activation, z [rows, I]
   GemmParams p{};
@@ -165,18 +167,23 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   p.ws_stride = static_cast<int64_t>(R / 128) * (H / 128);
   p.K = H;
   p.inter = I;
-  p.n_tiles = I / gemm_tile_n(GEMM_Z_ROUTED, fp8, gated, bm);
+  const int bn1 = gemm_tile_n(GEMM_Z_ROUTED, fp8, gated, bm, I);
+  p.n_tiles = I / bn1;
   p.sorted = sorted;
   p.block_expert = block_expert;
   p.ntp = ntp;
   p.T = T;
   p.top_k = top_k;
+  p.align_bm = bm;
   p.out = z;
   p.out_scale = zs;
   p.ldo = I;
-  launch(GEMM_Z_ROUTED, bm, p, cp.block_cap);
+  launch(GEMM_Z_ROUTED, bm, bn1, p, cp.block_cap);
   se.mark(4);
-  // routed second GEMM: z rows -> fused_expert_output[sorted row]
+  // routed second GEMM: z rows -> fused_expert_output[sorted row].  z is
+  // read row-contiguously, so the tile may be half an align block: 256-row
+  // blocks use 128-row tiles here (twice the workgroups over H).
+  const int bm2 = (!fp8 && bm == 256) ? 128 : bm;
   GemmParams q{};
   q.a = static_cast<const uint8_t*>(z);
   q.a_scale = zs;
@@ -186,15 +193,17 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   q.ws_stride = static_cast<int64_t>(H / 128) * (I / 128);
   q.K = I;
   q.inter = 0;
-  q.n_tiles = H / gemm_tile_n(GEMM_Y_ROUTED, fp8, gated, bm);
+  const int bn2 = gemm_tile_n(GEMM_Y_ROUTED, fp8, gated, bm2, H);
+  q.n_tiles = H / bn2;
   q.sorted = sorted;
   q.block_expert = block_expert;
   q.ntp = ntp;
   q.T = T;
   q.top_k = top_k;
+  q.align_bm = bm;
   q.out = feo;
   q.ldo = H;
-  launch(GEMM_Y_ROUTED, bm, q, cp.block_cap);
+  launch(GEMM_Y_ROUTED, bm2, bn2, q, cp.block_cap * (bm / bm2));
   se.mark(5);
   if (w->shared_inter > 0) {
     const int Is = w->shared_inter;
@@ -208,26 +217,30 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
     d.w_scale = w->shared_w13_scale;
     d.K = H;
     d.inter = Is;
-    d.n_tiles = Is / gemm_tile_n(GEMM_Z_DENSE, fp8, gated, dbm);
+    const int bn3 = gemm_tile_n(GEMM_Z_DENSE, fp8, gated, dbm, Is);
+    d.n_tiles = Is / bn3;
     d.T = T;
     d.top_k = 1;
+    d.align_bm = dbm;
     d.out = zsh;
     d.out_scale = zshs;
     d.ldo = Is;
     (void)Rs;
-    launch(GEMM_Z_DENSE, dbm, d, mblk);
+    launch(GEMM_Z_DENSE, dbm, bn3, d, mblk);
     GemmParams e{};
     e.a = static_cast<const uint8_t*>(zsh);
     e.a_scale = zshs;
     e.w = static_cast<const uint8_t*>(w->shared_w2);
     e.w_scale = w->shared_w2_scale;
     e.K = Is;
-    e.n_tiles = H / gemm_tile_n(GEMM_Y_DENSE, fp8, gated, dbm);
+    const int bn4 = gemm_tile_n(GEMM_Y_DENSE, fp8, gated, dbm, H);
+    e.n_tiles = H / bn4;
     e.T = T;
     e.top_k = 1;
+    e.align_bm = dbm;
     e.out = shared_out;
     e.ldo = H;
-    launch(GEMM_Y_DENSE, dbm, e, mblk);
+    launch(GEMM_Y_DENSE, dbm, bn4, e, mblk);
   }
   se.mark(6);
   return check_launch("moe_experts");
@@ -250,13 +263,17 @@ const char* moe_status_str(int status) {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_pick_block_m(int T, int top_k, int num_experts) {
+// Block size by average rows per expert, from sweeps on MI355X over the
+// Mixtral/DeepSeek/Llama-4 shapes: skinny experts want short tiles (weight
+// streaming, more workgroups); from ~100 rows the 8-wave 256-row bf16 tile
+// wins even with padding; fp8 tiles stop at 128 rows.
+int moe_pick_block_m(int T, int top_k, int num_experts, int quant) {
   if (T <= 0 || top_k <= 0 || num_experts <= 0) return 16;
   const int64_t avg = (static_cast<int64_t>(T) * top_k + num_experts - 1) / num_experts;
   if (avg <= 16) return 16;
   if (avg <= 32) return 32;
-  if (avg <= 96) return 64;
-  return 128;
+  if (quant == MOE_QUANT_FP8_G128) return avg <= 96 ? 64 : 128;
+  return avg <= 64 ? 64 : 256;
 }
 
 int moe_route(const float* logits, int T, int E, int top_k, int scoring, int renormalize,
@@ -471,7 +488,7 @@ size_t moe_forward_workspace_bytes(int T, int H, int top_k, const moe_weights* w
                                    int activation, int block_m, int apply_router_weight_on_input) {
   if (!weights || T < 0 || top_k < 1) return 0;
   if (check_weights(weights, H, activation, false) != MOE_OK) return 0;
-  const int bm = block_m ? block_m : moe_pick_block_m(T, top_k, weights->num_experts);
+  const int bm = block_m ? block_m : moe_pick_block_m(T, top_k, weights->num_experts, weights->quant);
   if (!valid_block_m(bm)) return 0;
   ForwardLayout L;
   return forward_layout(T, H, top_k, weights, bm, apply_router_weight_on_input, nullptr, &L);
@@ -497,7 +514,7 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
   if (H > 16384) return fail(MOE_ERR_INVALID_ARG, "H=%d > 16384", H);
   if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
   if (static_cast<int64_t>(T) * top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
-  const int bm = block_m ? block_m : moe_pick_block_m(T, top_k, E);
+  const int bm = block_m ? block_m : moe_pick_block_m(T, top_k, E, weights->quant);
   if (!valid_block_m(bm)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", bm);
   const bool fp8 = weights->quant == MOE_QUANT_FP8_G128;
   if (fp8 && bm > 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts support block_m <= 128");

@@ -36,6 +36,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Hardware float32 -> bf16 (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t f32_to_bf16_hw(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
@@ -84,10 +89,16 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// silu(v) = v / (1 + exp(-v)) with the accurate expf: on the fp8 path z is
-// re-quantised, and a closer z flips fewer codes at rounding edges.
+// silu(v) = v / (1 + exp(-v)) with the accurate expf (finalize-side users).
 __device__ __forceinline__ float silu(float v) {
   return v / (1.0f + expf(-v));
+}
+
+// GEMM-epilogue silu: v * rcp(1 + 2^(-v*log2 e)) on the hardware exp2/rcp
+// (about 1 ulp each; the epilogue runs it on every element of a tile).
+__device__ __forceinline__ float silu_fast(float v) {
+  const float e = __builtin_amdgcn_exp2f(-v * 1.4426950408889634f);
+  return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 }  // namespace moe

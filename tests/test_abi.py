@@ -53,15 +53,18 @@ def test_align_capacity_matches_oracle(moe, T, k, E, BM):
 
 def test_pick_block_m(moe):
     assert moe.moe_pick_block_m(1, 2, 8) == 16
-    assert moe.moe_pick_block_m(4096, 2, 8) == 128
-    assert moe.moe_pick_block_m(64, 8, 256) == 16
-    assert moe.moe_pick_block_m(8192, 8, 256) == 128
+    assert moe.moe_pick_block_m(512, 2, 8) == 256
+    assert moe.moe_pick_block_m(256, 2, 8) == 64
+    assert moe.moe_pick_block_m(4096, 2, 8) == 256
+    assert moe.moe_pick_block_m(4096, 2, 8, "fp8") == 128
+    assert moe.moe_pick_block_m(64, 8, 256, "fp8") == 16
+    assert moe.moe_pick_block_m(8192, 8, 256, "fp8") == 128
 
 
 def test_align_workspace_is_zero_for_one_tile(moe):
     lib = moe.binding.lib()
     assert lib.moe_align_workspace_bytes(16, 2, 8, 16) == 0
-    assert lib.moe_align_workspace_bytes(8192, 8, 256, 16) == 16 * 256 * 4
+    assert lib.moe_align_workspace_bytes(8192, 8, 256, 16) == 64 * 256 * 4
 
 
 def _bad(moe, fn, *args):

@@ -249,7 +249,7 @@ def test_forward_full_size_sampled(spec):
     moe = _moe()
     d, hw = _full_inputs(spec)
     w = _weights(moe, d)
-    bm = moe.moe_pick_block_m(spec.T, spec.top_k, spec.E)
+    bm = moe.moe_pick_block_m(spec.T, spec.top_k, spec.E, spec.quant)
     out, scale, _ = moe.moe_forward(d["x"], d["logits"], w, spec.top_k, spec.scoring,
                                     spec.renormalize, spec.apply_router_weight_on_input,
                                     spec.activation, 0, d.get("residual"), d.get("gamma"), spec.eps,
