@@ -28,15 +28,57 @@ def f64_of_fp8(codes, scales):
     return codecs.e4m3_decode(codes) * np.repeat(np.asarray(scales, np.float64), 128, axis=-1)
 
 
-def check_tolerance(got, ref_exact, ref_mirrored, path, what="", elementwise=True):
+def bf16_ulp(x):
+    """Spacing of bf16 numbers just above |x| (x already bf16-representable):
+    the size of a one-step rounding flip of that value."""
+    x = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
+    return np.where(x > 0, np.exp2(e - 7), np.exp2(-133.0))
+
+
+def finalize_flip_allowance(ref, gamma_bits=None):
+    """Per-output-element size of the rounding flips that the pages' bf16
+    boundaries allow, from the mirrored oracle's forward() dict.
+
+    Every routed row y[t, j] (and the shared row) is rounded to bf16 before
+    the weighted reduction.  Two correct implementations accumulate the
+    GEMM in different orders, so a value that lands within rounding error of
+    a bf16 midpoint may round either way: y[t, j, h] may differ by one bf16
+    step.  The reduction then moves by sum_j |w[t, j]| * ulp(y[t, j, h])
+    (+ ulp of the shared row), scaled by the RMSNorm factor when gamma is
+    given, and the final bf16 rounding adds one more step of the output.
+    Where the reduction cancels, this is larger than 5 % of the result."""
+    tok = ref["tokens"]
+    y = f64_of_bf16(ref["fused_expert_output"])[tok]            # [n, k, H]
+    w = np.abs(np.asarray(ref["topk_weights"], np.float64)[tok])  # [n, k]
+    acc = (w[:, :, None] * bf16_ulp(y)).sum(axis=1)
+    if ref.get("shared_out") is not None:
+        acc += bf16_ulp(f64_of_bf16(ref["shared_out"])[tok])
+    if gamma_bits is not None:
+        racc = f64_of_bf16(ref["residual_out"])
+        racc = racc[tok] if racc.shape[0] != tok.size else racc
+        r = 1.0 / np.sqrt((racc * racc).mean(axis=1, keepdims=True) + 1e-12)
+        acc = acc * r * np.abs(f64_of_bf16(gamma_bits))[None, :]
+    return acc
+
+
+def check_tolerance(got, ref_exact, ref_mirrored, path, what="", elementwise=True,
+                    min_identical=None, allowance=None):
     """The parity bar for floating-point outputs: max-norm bound against both
     oracle modes, per-element relative bound against the mirrored mode.
+
+    Per element (where |ref| > 1e-2): |got - ref| <= 5e-2 * |ref| + allowance,
+    where ``allowance`` (default 0) is the size of the one-step bf16 rounding
+    flips of intermediates that the pages fix in bf16 (finalize_flip_allowance).
 
     elementwise=False drops the per-element bound: used for end-to-end
     outputs downstream of the fp8 re-quantisation of the intermediate z,
     where two correct results legitimately differ by whole fp8 code steps at
     rounding edges; there the per-element bound is checked stage by stage
-    (z codes within one step, GEMM-2 against the z it consumed)."""
+    (z codes within one step, GEMM-2 against the z it consumed).
+
+    min_identical: if given, at least this fraction of elements must equal
+    the mirrored oracle exactly (the bf16 path mirrors every rounding)."""
     bound = BF16_BOUND if path == "bf16" else FP8_BOUND
     got = np.asarray(got, np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
@@ -51,11 +93,21 @@ def check_tolerance(got, ref_exact, ref_mirrored, path, what="", elementwise=Tru
         assert err <= bound * m + 1e-30, f"{what}: max|err| {err:.3g} > {bound} * max|ref| {m:.3g} ({name})"
     if elementwise and ref_mirrored is not None and np.asarray(ref_mirrored).size:
         ref = np.asarray(ref_mirrored, np.float64)
+        allow = np.zeros_like(ref) if allowance is None else np.broadcast_to(allowance, ref.shape)
         mask = np.abs(ref) > ELEM_FLOOR
         if mask.any():
-            rel = np.abs(got - ref)[mask] / np.abs(ref)[mask]
-            report["elem_rel"] = rel.max()
-            assert rel.max() <= ELEM_REL, f"{what}: per-element rel err {rel.max():.3g} > {ELEM_REL}"
+            err = np.abs(got - ref)[mask]
+            lim = ELEM_REL * np.abs(ref)[mask] + allow[mask]
+            worst = int(np.argmax(err / lim))
+            report["elem_rel"] = float((err / np.abs(ref)[mask]).max())
+            report["elem_frac_of_limit"] = float(err[worst] / lim[worst])
+            assert np.all(err <= lim), (
+                f"{what}: per-element err {err[worst]:.3g} > limit {lim[worst]:.3g} "
+                f"(ref {ref[mask][worst]:.4g}, got {got[mask][worst]:.4g})")
+    if min_identical is not None and ref_mirrored is not None and np.asarray(ref_mirrored).size:
+        same = float((got == np.asarray(ref_mirrored, np.float64)).mean())
+        report["identical"] = same
+        assert same >= min_identical, f"{what}: only {same:.3f} of elements equal the mirrored oracle"
     return report
 
 
