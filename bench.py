@@ -35,11 +35,84 @@ def parse():
                     help="family@T<tokens>, e.g. mixtral@T4096, deepseek_v3@T8192, llama4@T2048")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=512,
+    ap.add_argument("--cpu-sample", type=int, default=3072,
                     help="tokens in the oracle's timed sample (about 10-30 s of CPU work)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 counters (json)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after the timed steps, run a plain fp32 copy kernel (y = x * 1) over "
+                         "BYTES bytes three times: the reference launch that scales the HBM "
+                         "byte counters")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: read two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) "
+                         "of a --copy-calibration run and record the routed GEMM-1 traffic "
+                         "for --workload in --traffic")
     return ap.parse_args()
+
+
+# Routed GEMM-1: the grouped GEMM instantiated with A_GATHER (0) and EPI_Z (0).
+GEMM1_KERNEL_RE = r"grouped_gemm_kernel<.*GemmCfg<(-?\d+, ){5}(true|false), (true|false), 0, 0,"
+COPY_KERNEL_RE = r"elementwise|vectorized"
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP sources: counters taken on other kernels are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_routing_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _pmc_means(run_dir, counter):
+    """Per-dispatch mean of one counter for the GEMM-1 and copy kernels."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    gemm1, copies = [], []
+    for fn in files:
+        for r in csv.DictReader(open(fn)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if re.search(GEMM1_KERNEL_RE, name):
+                gemm1.append(v)
+            elif re.search(COPY_KERNEL_RE, name):
+                copies.append((int(r["Dispatch_Id"]), v))
+    # the calibration copies are the last three elementwise launches of the run
+    copies = [v for _, v in sorted(copies)[-3:]]
+    if not gemm1 or len(copies) < 3:
+        raise SystemExit(f"{counter}: GEMM-1 or calibration dispatches missing in {run_dir}")
+    return sum(gemm1) / len(gemm1), sum(copies) / len(copies), len(copies)
+
+
+def write_traffic(a):
+    spec = find_spec(a.workload)
+    rec = {"kernel": "routed GEMM-1", "kernel_regex": GEMM1_KERNEL_RE,
+           "sources_sha256": kernel_sources_digest()}
+    total = 0.0
+    for counter, run_dir in (("FETCH_SIZE", a.write_traffic[0]), ("WRITE_SIZE", a.write_traffic[1])):
+        g_kib, c_kib, n = _pmc_means(run_dir, counter)
+        factor = c_kib * 1024.0 / a.copy_calibration     # counter bytes per true byte
+        rec[counter] = {"gemm1_kib_per_dispatch": round(g_kib, 1),
+                        "copy_kib_per_dispatch": round(c_kib, 1), "copy_dispatches": n,
+                        "copy_true_bytes": a.copy_calibration, "factor": round(factor, 4),
+                        "gemm1_bytes": round(g_kib * 1024.0 / factor)}
+        total += g_kib * 1024.0 / factor
+    rec["gemm1_bytes"] = round(total)
+    tr = {}
+    if os.path.exists(a.traffic):
+        tr = json.load(open(a.traffic))
+    tr[spec.name] = rec
+    with open(a.traffic, "w") as f:
+        json.dump(tr, f, indent=1)
+        f.write("\n")
+    print(json.dumps({spec.name: rec}))
 
 
 def find_spec(name):
@@ -96,6 +169,11 @@ def cpu_baseline(spec, d, sample_n):
 
 def main():
     a = parse()
+    if a.write_traffic:
+        if a.copy_calibration <= 0:
+            raise SystemExit("--write-traffic needs --copy-calibration BYTES of the profiled run")
+        write_traffic(a)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(multi-GPU sharding is a design note, not implemented)"}))
@@ -145,8 +223,9 @@ def main():
     traffic = None
     if os.path.exists(a.traffic):
         try:
-            tr = json.load(open(a.traffic))
-            traffic = tr.get(spec.name, {}).get("gemm1_bytes")
+            rec = json.load(open(a.traffic)).get(spec.name, {})
+            if rec.get("sources_sha256") == kernel_sources_digest():
+                traffic = rec.get("gemm1_bytes")
         except Exception:
             traffic = None
     line = {
@@ -175,6 +254,14 @@ def main():
                      "unit": "TFLOP/s", "frac": round(g1_tflops / PEAK_TFLOPS[dtype], 4),
                      "traffic": traffic},
     }
+    if a.copy_calibration:
+        n = a.copy_calibration // 4
+        cx = torch.ones(n, dtype=torch.float32, device=dev)
+        cy = torch.empty_like(cx)
+        for _ in range(3):
+            torch.mul(cx, 1.0, out=cy)
+        torch.cuda.synchronize()
+        del cx, cy
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(spec, d, a.cpu_sample)
     print(json.dumps(line), flush=True)
