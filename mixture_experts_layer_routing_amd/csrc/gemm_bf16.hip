@@ -12,14 +12,14 @@
 
 namespace moe {
 
-// LDS stages per tile.  Measured on MI355X (Mixtral-shaped GEMMs): a third
-// or fourth stage costs more in occupancy (fewer resident workgroups) than
-// it gains in latency hiding at every tile size tried, so two it is.
-constexpr int bf16_stages(int bm, int nb) {
-  (void)bm;
-  (void)nb;
-  return 2;
-}
+// k-tile geometry: 128-byte k-tiles (64 bf16) in two LDS stages for every
+// tile.  Measured on MI355X with Mixtral-shaped GEMMs: 64-byte k-tiles in
+// four or five stages (twice the bytes in flight in the same LDS) run
+// 10-35 % slower than two 128-byte stages -- the half-line requests cost
+// more than the deeper pipeline gains -- and a third 128-byte stage does not
+// fit beside a 256 x 512-row tile, or costs a resident workgroup at 128 rows.
+constexpr int bf16_rb(int bm) { return (void)bm, 128; }
+constexpr int bf16_stages(int bm, int nb) { return (void)bm, (void)nb, 2; }
 
 // Wave grid of the 256-row tiles: 8 waves (2 per SIMD), each 128 rows x a
 // quarter of the tile's columns; two waves per SIMD let one issue MFMAs
@@ -29,7 +29,7 @@ constexpr int kW128M = 2, kW128N = 4;
 
 template <int BM, int BNZ, int WM, int WN, int MF, bool GATED, int AM, int EP>
 using Bf16Cfg = GemmCfg<BM, BNZ, WM, WN, MF, false, GATED, AM, EP,
-                        bf16_stages(BM, GATED ? 2 * BNZ : BNZ)>;
+                        bf16_stages(BM, GATED ? 2 * BNZ : BNZ), bf16_rb(BM)>;
 
 template <int AM, int EP, bool GATED>
 static void dispatch_bm(int block_m, int bnz, const GemmParams& p, int64_t max_mblk,

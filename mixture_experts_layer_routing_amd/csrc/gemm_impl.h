@@ -9,15 +9,18 @@
 //
 // Tiling: 4 or 8 waves, tile BM x NB (NB = 2*BNZ when gated: BNZ
 // gate rows n0.. and the matching BNZ up rows I+n0.., so SiLU-mul is
-// elementwise in registers).  Each k-tile is 128 bytes of K per row (64 bf16
-// or 128 fp8 elements), moved global -> LDS by direct-to-LDS loads
-// (global_load_lds_dwordx4: no staging registers, no ds_write), double-
-// buffered with one barrier per k-tile; the next tile's loads are in flight
-// while the current one feeds the MFMAs.  LDS rows are 128 B with the 16-byte
-// chunk index XOR-swizzled by (row >> 1) & 7, so the fragment reads (16
-// lanes = 16 rows at one chunk column) hit all 64 banks; a direct load writes 64 lanes x
-// 16 B contiguously, so each lane fetches the global chunk that belongs in
-// its slot.  Fragments whose rows are all padding skip their MFMAs.
+// elementwise in registers).  Each k-tile is RB bytes of K per row (128: 64
+// bf16 or 128 fp8 elements; 64: 32 bf16), moved global -> LDS by
+// direct-to-LDS loads (global_load_lds_dwordx4: no staging registers, no
+// ds_write) into a ring of NSTAGE LDS stages with one barrier per k-tile:
+// NSTAGE-1 k-tiles of loads are in flight while one feeds the MFMAs.  The
+// barrier is a bare s_barrier (lds_barrier): __syncthreads() would also wait
+// for the loads still in flight.  The 16-byte
+// chunk index of each LDS row is XOR-swizzled so that the fragment reads
+// (16 lanes = 16 rows at one chunk column) hit all 64 banks; a direct load
+// writes 64 lanes x 16 B contiguously, so each lane fetches the global chunk
+// that belongs in its slot.  Fragments whose rows are all padding skip their
+// MFMAs.
 //
 // MFMA: bf16 v_mfma_f32_32x32x16_bf16 / 16x16x32_bf16; fp8 E4M3
 // v_mfma_f32_32x32x64_f8f6f4 / 16x16x128_f8f6f4.  Operand lane layout: lane l
@@ -47,7 +50,7 @@ enum { A_GATHER = 0, A_ROWS = 1, A_DENSE = 2 };
 enum { EPI_Z = 0, EPI_OUT_ROUTED = 1, EPI_OUT_DENSE = 2 };
 
 template <int BM_, int BNZ_, int WAVES_M_, int WAVES_N_, int MF_, bool FP8_, bool GATED_,
-          int AMODE_, int EPI_, int NSTAGE_ = 2, int PF_ = -1>
+          int AMODE_, int EPI_, int NSTAGE_ = 2, int RB_ = 128>
 struct GemmCfg {
   static constexpr int BM = BM_, BNZ = BNZ_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, MF = MF_;
   static constexpr bool FP8 = FP8_, GATED = GATED_;
@@ -55,21 +58,25 @@ struct GemmCfg {
   // LDS stages: NSTAGE-1 k-tiles of direct-to-LDS loads in flight while
   // one is consumed (one barrier per k-tile either way).
   static constexpr int NSTAGE = NSTAGE_;
-  // L2 prefetch distance in k-tiles (0 = off, -1 = the library default).
-  static constexpr int PF = PF_;
+  // Bytes of K per row in one k-tile: 128, or 64 (bf16 only).
+  static constexpr int RB = RB_;
 };
 
-// Default L2 prefetch distance (k-tiles ahead of the one being consumed).
-constexpr int kDefaultPrefetch = 0;
-
 // gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16 lanes per
-// cycle (256 B).  Rows are 128 B, so rows r and r+2 share banks; XOR-ing the
+// cycle (256 B).  128-byte rows: rows r and r+2 share banks, and XOR-ing the
 // chunk with (row >> 1) & 7 gives the 8 rows of each parity among 16
-// consecutive rows 8 distinct chunks, so a fragment read (16 lanes = 16
+// consecutive rows 8 distinct chunks.  64-byte rows: rows r and r+4 share
+// banks, and XOR-ing with (row >> 2) & 3 gives the 4 rows of each residue
+// mod 4 distinct chunks.  Either way a fragment read (16 lanes = 16
 // consecutive rows at one chunk column) touches all 64 banks once.
-__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+template <int RB>
+__device__ __forceinline__ int swz_key(int row) {
+  static_assert(RB == 128 || RB == 64, "row bytes");
+  return RB == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
+template <int RB>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ swz_key(row)) << 4);
+  return row * RB + ((chunk ^ swz_key<RB>(row)) << 4);
 }
 
 template <int MF, bool FP8>
@@ -79,9 +86,10 @@ template <>
 struct Mfma<32, false> {
   typedef f32x16 acc_t;
   typedef u32x4 frag_t;
-  static constexpr int NSUB = 4, NACC = 16;
+  static constexpr int KSTEP = 32, NACC = 16;  // bytes of K per MFMA
+  template <int RB>
   __device__ static frag_t read(const uint8_t* base, int row, int s, int lane) {
-    return *reinterpret_cast<const u32x4*>(base + swz(row, 2 * s + (lane >> 5)));
+    return *reinterpret_cast<const u32x4*>(base + swz<RB>(row, 2 * s + (lane >> 5)));
   }
   __device__ static acc_t mma(const frag_t& a, const frag_t& b, const acc_t& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -93,9 +101,10 @@ template <>
 struct Mfma<16, false> {
   typedef f32x4 acc_t;
   typedef u32x4 frag_t;
-  static constexpr int NSUB = 2, NACC = 4;
+  static constexpr int KSTEP = 64, NACC = 4;
+  template <int RB>
   __device__ static frag_t read(const uint8_t* base, int row, int s, int lane) {
-    return *reinterpret_cast<const u32x4*>(base + swz(row, 4 * s + (lane >> 4)));
+    return *reinterpret_cast<const u32x4*>(base + swz<RB>(row, 4 * s + (lane >> 4)));
   }
   __device__ static acc_t mma(const frag_t& a, const frag_t& b, const acc_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -107,11 +116,12 @@ template <>
 struct Mfma<32, true> {
   typedef f32x16 acc_t;
   typedef i32x8 frag_t;
-  static constexpr int NSUB = 2, NACC = 16;
+  static constexpr int KSTEP = 64, NACC = 16;
+  template <int RB>
   __device__ static frag_t read(const uint8_t* base, int row, int s, int lane) {
     const int c0 = 4 * s + 2 * (lane >> 5);
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz(row, c0));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz(row, c0 + 1));
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz<RB>(row, c0));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz<RB>(row, c0 + 1));
     frag_t f;
     f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
     f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
@@ -126,11 +136,12 @@ template <>
 struct Mfma<16, true> {
   typedef f32x4 acc_t;
   typedef i32x8 frag_t;
-  static constexpr int NSUB = 1, NACC = 4;
+  static constexpr int KSTEP = 128, NACC = 4;
+  template <int RB>
   __device__ static frag_t read(const uint8_t* base, int row, int s, int lane) {
     const int c0 = 2 * (lane >> 4);
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz(row, c0));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz(row, c0 + 1));
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz<RB>(row, c0));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz<RB>(row, c0 + 1));
     frag_t f;
     f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
     f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
@@ -162,12 +173,18 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
 
-// L2 prefetch: one 4-byte direct-to-LDS load per lane into a 256-byte sink
-// (contents discarded) pulls each lane's 128-byte line into the caches
-// without tying up a VGPR.
-__device__ __forceinline__ void l2_prefetch_line(const uint8_t* g, uint8_t* sink) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)sink, 4, 0, 0);
+// Workgroup barrier for the k-loop.  __syncthreads() (and a workgroup
+// fence, even one restricted to LDS) makes every wave wait for all of its
+// outstanding global loads (vmcnt(0)) before arriving; that includes the
+// direct-to-LDS loads of the later stages and would cut the pipeline to one
+// k-tile in flight.  Here the caller has already waited for its own loads of
+// the stage about to be read (s_waitcnt vmcnt(N)); lgkmcnt(0) completes this
+// wave's LDS reads and writes, and the "memory" clobbers keep the compiler
+// from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Wait for every outstanding global (and direct-to-LDS) load of this wave.
@@ -194,29 +211,33 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
   constexpr int NT = 64 * NW;                     // threads per workgroup
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(FM >= 1 && FN >= 1 && WM % MF == 0 && WN % MF == 0, "wave tile");
-  constexpr int A_BYTES = BM * 128, B_BYTES = NB * 128, STAGE = A_BYTES + B_BYTES;
+  constexpr int RB = C::RB;
+  static_assert(RB == 128 || (RB == 64 && !FP8), "fp8 k-tiles are one 128-wide scale block");
+  constexpr int A_BYTES = BM * RB, B_BYTES = NB * RB, STAGE = A_BYTES + B_BYTES;
   constexpr int ROWS = BM + NB;           // LDS rows per stage: A rows, then B rows
-  static_assert(ROWS % 8 == 0, "8-row load groups");
-  constexpr int NI = ROWS / 8;            // 1 KB direct-to-LDS loads per k-tile
+  constexpr int LPR = RB / 16;            // lanes per row in one 1 KB direct load
+  constexpr int RPG = 64 / LPR;           // rows per load group
+  static_assert(ROWS % RPG == 0, "whole load groups");
+  constexpr int NI = ROWS / RPG;          // 1 KB direct-to-LDS loads per k-tile
   constexpr int NIW = (NI + NW - 1) / NW; // ... per wave (at most)
   constexpr int EB = FP8 ? 1 : 2;
   typedef Mfma<MF, FP8> M;
   typedef typename M::acc_t acc_t;
   typedef typename M::frag_t frag_t;
-  constexpr int NSUB = M::NSUB, NACC = M::NACC;
+  constexpr int NSUB = RB / M::KSTEP, NACC = M::NACC;
+  static_assert(NSUB >= 1, "k-tile holds at least one MFMA step");
   constexpr int EPI_BYTES = (C::EPI == EPI_Z && FP8) ? BM * BNZ * 4 : BM * BNZ * 2;
   constexpr int NSTAGE = C::NSTAGE;
-  constexpr int PF = C::PF < 0 ? kDefaultPrefetch : C::PF;
-  static_assert(PF == 0 || NSTAGE == 2, "L2 prefetch runs with two LDS stages");
-  constexpr int PFI = PF > 0 ? (ROWS / 64 + NW - 1) / NW : 0;  // prefetch loads per wave per k-tile
   static_assert(NSTAGE == 2 || (!FP8 && NI % NW == 0), "deeper pipelines: bf16, whole load groups");
-  constexpr int SMEM = cmax(NSTAGE * STAGE, EPI_BYTES);
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
-  __shared__ float sA[FP8 ? 2 * BM : 1];
-  __shared__ __attribute__((aligned(16))) uint8_t pf_sink[256];
-  // fp8: the tile's weight-block scales along K (gate row, then up row)
+  constexpr int SMEM_TILE = cmax(NSTAGE * STAGE, EPI_BYTES);
+  // fp8 only, after the stages: the activation scales of two k-tiles
+  // (sA) and the tile's weight-block scales along K (sW: gate row, then up
+  // row).  bf16 tiles use every byte of the 160 KB for stages.
   constexpr int kMaxKB = 128;  // K <= 16384
-  __shared__ float sW[FP8 ? 2 * kMaxKB : 1];
+  constexpr int SCALE_BYTES = FP8 ? (2 * BM + 2 * kMaxKB) * 4 : 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_TILE + SCALE_BYTES];
+  float* const sA = reinterpret_cast<float*>(smem + SMEM_TILE);
+  float* const sW = sA + 2 * BM;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -257,22 +278,32 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
   if constexpr (C::AMODE == A_DENSE) {
     valid_rows = min(BM, p.T - m0);
   } else {
+    // one row per thread; the per-wave counts meet in the first bytes of
+    // smem, which the stage loads only overwrite after the second barrier
+    static_assert(BM <= NT, "one row per thread");
+    const bool live = tid < BM && p.sorted[m0 + tid] < nflat;
+    int* const red = reinterpret_cast<int*>(smem);
+    const int wcount = __builtin_popcountll(__ballot(live));
+    if (lane == 0) red[wave] = wcount;
+    __syncthreads();
     int v = 0;
-    for (int r = tid; r < BM; r += NT) v += p.sorted[m0 + r] < nflat ? 1 : 0;
-    valid_rows = __syncthreads_count(v);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[w];
+    __syncthreads();
+    valid_rows = v;
     if (valid_rows == 0) return;  // a tile past its expert's rows (block-uniform)
   }
 
   // ---- direct-to-LDS source pointers ----
-  // Load group j covers LDS rows 8j..8j+7 of a stage; lane i fills the
-  // 16-byte slot i of the group, i.e. row 8j + i/8 at physical chunk i%8,
-  // which holds logical chunk (i%8) ^ swz_key(row).
+  // Load group j covers LDS rows RPG*j.. of a stage; lane i fills the
+  // 16-byte slot i of the group, i.e. row RPG*j + i/LPR at physical chunk
+  // i%LPR, which holds logical chunk (i%LPR) ^ swz_key(row).
   const uint8_t* src[NIW];
 #pragma unroll
   for (int s = 0; s < NIW; ++s) {
     const int j = wave + NW * s;
-    const int r = 8 * j + (lane >> 3);
-    const int lchunk = (lane & 7) ^ swz_key(r);
+    const int r = RPG * j + lane / LPR;
+    const int lchunk = (lane % LPR) ^ swz_key<RB>(r);
     const uint8_t* ptr = p.a;  // any valid row; unused when j >= NI
     if (j < NI) {
       if (r < BM) {
@@ -295,33 +326,6 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
       }
     }
     src[s] = ptr + lchunk * 16;
-  }
-  // L2 prefetch rows: load u of this wave covers tile rows 64*(wave + NW*u)
-  // + lane (A rows, then B rows; past the end it repeats row 0).
-  const uint8_t* pf_src[PFI > 0 ? PFI : 1];
-#pragma unroll
-  for (int u = 0; u < PFI; ++u) {
-    const int r = 64 * (wave + NW * u) + lane;
-    const uint8_t* ptr = p.a;
-    if (r < BM) {
-      int srow = 0;
-      if constexpr (C::AMODE == A_GATHER) {
-        const int sid = p.sorted[m0 + r];
-        srow = sid < nflat ? sid / p.top_k : 0;
-      } else if constexpr (C::AMODE == A_ROWS) {
-        srow = m0 + r;
-      } else {
-        srow = min(m0 + r, p.T - 1);
-      }
-      ptr = p.a + static_cast<int64_t>(srow) * krow_bytes;
-    } else if (r < ROWS) {
-      const int b = r - BM;
-      int wrow;
-      if constexpr (C::GATED) wrow = b < BNZ ? n0 + b : p.inter + n0 + (b - BNZ);
-      else wrow = n0 + b;
-      ptr = wbase + static_cast<int64_t>(wrow) * krow_bytes;
-    }
-    pf_src[u] = ptr;
   }
   // fp8: this thread's activation-scale row (threads < BM) and the weight-scale rows
   static_assert(!FP8 || BM <= NT, "one activation-scale row per thread");
@@ -348,16 +352,12 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
     // made visible by the first k-tile's barrier
   }
 
-  auto prefetch = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < PFI; ++u) l2_prefetch_line(pf_src[u] + static_cast<int64_t>(kt) * 128, pf_sink);
-  };
   auto dma = [&](int kt, int buf) {
 #pragma unroll
     for (int s = 0; s < NIW; ++s) {
       const int j = wave + NW * s;
       if (NI % NW == 0 || j < NI)
-        lds_dma16(src[s] + static_cast<int64_t>(kt) * 128, smem + buf * STAGE + j * 1024);
+        lds_dma16(src[s] + static_cast<int64_t>(kt) * RB, smem + buf * STAGE + j * 1024);
     }
   };
 
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
 #pragma unroll
         for (int v = 0; v < NACC; ++v) acc[g][fm][fn][v] = 0.f;
 
-  const int nk = p.K / (128 / EB);
+  const int nk = p.K / (RB / EB);
   const int row_w = wm * WM;
   // fragments of this wave that hold at least one data row (wave-uniform)
   const int fm_live = __builtin_amdgcn_readfirstlane(
@@ -398,21 +398,15 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
       if constexpr (NSTAGE > 2) {
         if (kt + NSTAGE - 2 < nk) wait_vm_loads_but<NIW * (NSTAGE - 2)>();
         else wait_vm_loads();
-      } else if constexpr (PF > 0) {
-        // the prefetch issued after this k-tile's DMA may stay in flight
-        if (kt >= 1 && kt - 1 + PF < nk) wait_vm_loads_but<PFI>();
-        else wait_vm_loads();
       } else {
         wait_vm_loads();
       }
-      __syncthreads();
+      lds_barrier();
       if (kt + NSTAGE - 1 < nk) {
         if constexpr (FP8)
           if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kt + 1];
         dma(kt + NSTAGE - 1, nbuf);
       }
-      if constexpr (PF > 0)
-        if (kt + PF < nk) prefetch(kt + PF);
       const uint8_t* As = smem + buf * STAGE;
       const uint8_t* Bs = As + A_BYTES;
       if constexpr (!FP8) {
@@ -423,12 +417,12 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm)
             if (FULL || fm < fm_live)
-              fa[set][fm] = M::read(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+              fa[set][fm] = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
 #pragma unroll
           for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-              fb[set][g][fn] = M::read(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+              fb[set][g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
         };
         rd(0, 0);
 #pragma unroll
@@ -468,12 +462,12 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
           frag_t fa[FM], fb[G][FN];
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm)
-            if (FULL || fm < fm_live) fa[fm] = M::read(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+            if (FULL || fm < fm_live) fa[fm] = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
 #pragma unroll
           for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-              fb[g][fn] = M::read(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+              fb[g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm)
             if (FULL || fm < fm_live)
