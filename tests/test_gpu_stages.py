@@ -147,7 +147,8 @@ def test_align_bit_exact_on_config_routing(spec, BM):
 @pytest.mark.parametrize("T,k,E,BM,pattern", [
     (5000, 1, 8, 16, "one_expert"), (9000, 8, 256, 32, "hot"), (4096, 1, 16, 256, "random"),
     (4097, 1, 16, 64, "random"), (1, 2, 8, 16, "random"), (0, 2, 8, 16, "random"),
-    (20000, 4, 1024, 128, "random"), (3000, 2, 3, 16, "empty")])
+    (20000, 4, 1024, 128, "random"), (3000, 2, 3, 16, "empty"),
+    (4096, 8, 256, 64, "random"), (4097, 8, 256, 64, "hot")])
 def test_align_adversarial(T, k, E, BM, pattern):
     _announce(f"align adversarial T={T} k={k} E={E} BM={BM} {pattern}")
     g = torch.Generator().manual_seed(T + E)
@@ -163,6 +164,17 @@ def test_align_adversarial(T, k, E, BM, pattern):
         ids[:, 1] = 2
         ids[:, 0] = 0
     _align_compare(ids.to(torch.int32).contiguous(), E, BM)
+
+
+@pytest.mark.parametrize("T,k,E,BM", [(20000, 8, 256, 128), (200000, 8, 256, 128),
+                                      (600000, 8, 64, 64), (2100000, 2, 8, 256)])
+def test_align_multi_tile_sizes(T, k, E, BM):
+    """Enough ids for several first-level scan blocks (over 64 tiles) and for
+    tiles above the 2048-id minimum."""
+    _announce(f"align large T={T} k={k} E={E} BM={BM}")
+    g = torch.Generator().manual_seed(T + E)
+    ids = torch.rand((T, E), generator=g).argsort(dim=1)[:, :k].to(torch.int32).contiguous()
+    _align_compare(ids, E, BM)
 
 
 def test_align_is_deterministic_across_runs():
