@@ -32,7 +32,9 @@ __device__ __forceinline__ void store8_bf16(uint16_t* p, const float* f) {
   *reinterpret_cast<u32x4*>(p) = o;
 }
 
-template <int MAXC, bool FP8OUT>
+// KT: top_k when it is one of the common 1, 2, 4, 8 (the row loads are then
+// unrolled and all issued before the first add), 0 for any other value.
+template <int MAXC, bool FP8OUT, int KT>
 __global__ __launch_bounds__(256) void finalize_kernel(
     void* __restrict__ output, float* __restrict__ out_scale,
     const uint16_t* __restrict__ y, const float* __restrict__ w, int top_k, int H,
@@ -50,12 +52,28 @@ __global__ __launch_bounds__(256) void finalize_kernel(
 #pragma unroll
     for (int v = 0; v < 8; ++v) acc[i][v] = 0.f;
     if (c < nch) {
-      for (int j = 0; j < top_k; ++j) {
-        const float wj = weight_on_input ? 1.0f : w[static_cast<size_t>(t) * top_k + j];
-        float f[8];
-        load8(y + (static_cast<size_t>(t) * top_k + j) * H + c * 8, f);
+      if constexpr (KT > 0) {
+        u32x4 r[KT];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) acc[i][v] += wj * f[v];
+        for (int j = 0; j < KT; ++j)
+          r[j] = *reinterpret_cast<const u32x4*>(y + (static_cast<size_t>(t) * KT + j) * H + c * 8);
+#pragma unroll
+        for (int j = 0; j < KT; ++j) {
+          const float wj = weight_on_input ? 1.0f : w[static_cast<size_t>(t) * KT + j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[i][2 * q] += wj * bf16_to_f32(r[j][q]);
+            acc[i][2 * q + 1] += wj * bf16_to_f32(r[j][q] >> 16);
+          }
+        }
+      } else {
+        for (int j = 0; j < top_k; ++j) {
+          const float wj = weight_on_input ? 1.0f : w[static_cast<size_t>(t) * top_k + j];
+          float f[8];
+          load8(y + (static_cast<size_t>(t) * top_k + j) * H + c * 8, f);
+#pragma unroll
+          for (int v = 0; v < 8; ++v) acc[i][v] += wj * f[v];
+        }
       }
       if (shared) {
         float f[8];
@@ -128,16 +146,29 @@ __global__ __launch_bounds__(256) void finalize_kernel(
   }
 }
 
+template <int MAXC, int KT>
+void launch_fin_k(void* out, float* out_scale, int out_quant, const uint16_t* y, const float* w,
+                  int T, int k, int H, int woi, const uint16_t* sh, const uint16_t* res,
+                  uint16_t* res_out, const uint16_t* gamma, float eps, hipStream_t s) {
+  if (out_quant == 1)
+    finalize_kernel<MAXC, true, KT><<<T, 256, 0, s>>>(out, out_scale, y, w, k, H, woi, sh, res,
+                                                      res_out, gamma, eps);
+  else
+    finalize_kernel<MAXC, false, KT><<<T, 256, 0, s>>>(out, out_scale, y, w, k, H, woi, sh, res,
+                                                       res_out, gamma, eps);
+}
+
 template <int MAXC>
 void launch_fin(void* out, float* out_scale, int out_quant, const uint16_t* y, const float* w,
                 int T, int k, int H, int woi, const uint16_t* sh, const uint16_t* res,
                 uint16_t* res_out, const uint16_t* gamma, float eps, hipStream_t s) {
-  if (out_quant == 1)
-    finalize_kernel<MAXC, true><<<T, 256, 0, s>>>(out, out_scale, y, w, k, H, woi, sh, res,
-                                                  res_out, gamma, eps);
-  else
-    finalize_kernel<MAXC, false><<<T, 256, 0, s>>>(out, out_scale, y, w, k, H, woi, sh, res,
-                                                   res_out, gamma, eps);
+  switch (k) {
+    case 1: launch_fin_k<MAXC, 1>(out, out_scale, out_quant, y, w, T, k, H, woi, sh, res, res_out, gamma, eps, s); break;
+    case 2: launch_fin_k<MAXC, 2>(out, out_scale, out_quant, y, w, T, k, H, woi, sh, res, res_out, gamma, eps, s); break;
+    case 4: launch_fin_k<MAXC, 4>(out, out_scale, out_quant, y, w, T, k, H, woi, sh, res, res_out, gamma, eps, s); break;
+    case 8: launch_fin_k<MAXC, 8>(out, out_scale, out_quant, y, w, T, k, H, woi, sh, res, res_out, gamma, eps, s); break;
+    default: launch_fin_k<MAXC, 0>(out, out_scale, out_quant, y, w, T, k, H, woi, sh, res, res_out, gamma, eps, s); break;
+  }
 }
 
 }  // namespace
