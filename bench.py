@@ -8,8 +8,9 @@ N(0, 2)) at T=4096 tokens.
 
 Prints ONE JSON line: tokens/s (value), TFLOP/s, per-stage times from HIP
 events recorded on the launch stream, the dominant kernel's roofline
-(routed GEMM-1, MFMA-bound) and the CPU oracle timed on a bounded token
-sample on this host ("cpu_baseline").
+(routed GEMM-1, MFMA-bound), the memory-bound stages' bandwidth (finalize
+at hidden 7168 with a cold cache, align over 2^24 ids) and the CPU oracle
+timed on a bounded token sample on this host ("cpu_baseline").
 """
 
 import argparse
@@ -35,7 +36,9 @@ def parse():
                     help="family@T<tokens>, e.g. mixtral@T4096, deepseek_v3@T8192, llama4@T2048")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=3072,
+    ap.add_argument("--no-hbm-stages", action="store_true",
+                    help="skip the finalize (hidden 7168) and align (2^24 ids) bandwidth legs")
+    ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens in the oracle's timed sample (about 10-30 s of CPU work)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 counters (json)")
@@ -167,6 +170,75 @@ def cpu_baseline(spec, d, sample_n):
                       f"numpy float64, mirrored mode, {dt:.1f} s"}
 
 
+def hbm_stages(torch, moe, dev):
+    """Memory-bound stages at the sizes where bandwidth, not launch latency,
+    is what they show: finalize on the hidden-7168 fusion shape (k=4,
+    shared + residual + RMSNorm, T=16384; bf16 and fp8 output) with two input
+    sets of 1.6 GB alternating, so every call reads from HBM rather than the
+    256 MB last-level cache; and align over 2^24 ids.  GB/s counts the bytes
+    the stage must move once (algorithmic), timed with HIP events over 20
+    back-to-back calls."""
+    from workloads import CONFIGS, make_finalize_inputs
+
+    def timed(fn, calls):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(calls):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / calls   # us
+
+    out = {}
+    spec = [s for s in CONFIGS["finalize"] if s.T == 16384 and s.out_quant == "none"][0]
+    sets = []
+    for r in range(2):
+        d = make_finalize_inputs(spec, device=dev) if r == 0 else \
+            {k: (v.clone() if torch.is_tensor(v) else v) for k, v in sets[0].items()}
+        sets.append(d)
+    T, k, H = spec.T, spec.top_k, spec.H
+    for oq in ("none", "fp8"):
+        outs = [torch.empty((T, H), dtype=torch.bfloat16 if oq == "none" else torch.uint8,
+                            device=dev) for _ in sets]
+        scs = [torch.empty((T, H // 128), dtype=torch.float32, device=dev) for _ in sets]
+
+        def fin(i, oq=oq, outs=outs, scs=scs):
+            d = sets[i % 2]
+            moe.moe_finalize(d["fused_expert_output"], d["topk_weights"], d["topk_ids"], False,
+                             d["shared"], d["residual"], d["gamma"], spec.eps, oq,
+                             output=outs[i % 2], output_scale=scs[i % 2] if oq == "fp8" else None)
+        us = timed(fin, 20)
+        per_tok = k * H * 2 + k * 4 + 2 * H * 2 + (H * 2 if oq == "none" else H + H // 128 * 4)
+        gbs = T * per_tok / us / 1e3
+        out["finalize" if oq == "none" else "finalize_fp8_out"] = {
+            "workload": f"finalize T={T} k={k} H={H} shared+residual+RMSNorm, {oq} out, cold",
+            "bytes_per_token": per_tok, "us": round(us, 2), "GB_s": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del sets
+    torch.cuda.empty_cache()
+    sweep = []
+    for E, kk, bm in ((8, 2, 256), (256, 8, 128)):
+        n = 1 << 24
+        g = torch.Generator(device=dev)
+        g.manual_seed(E)
+        ids = torch.randint(0, E, (n // kk, kk), device=dev, dtype=torch.int32, generator=g)
+        res = moe.moe_align(ids, E, bm)
+
+        def al(i, ids=ids, E=E, bm=bm):
+            moe.moe_align(ids, E, bm)
+        us = timed(al, 20)
+        alg = 4 * n + 4 * (res["sorted_token_ids"].numel() + res["block_expert_ids"].numel()) \
+            + 8 * E + 8
+        gbs = alg / us / 1e3
+        sweep.append({"n_ids": n, "E": E, "top_k": kk, "block_m": bm, "us": round(us, 2),
+                      "GB_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+        del ids, res
+    out["align_sweep"] = sweep
+    return out
+
+
 def main():
     a = parse()
     if a.write_traffic:
@@ -262,8 +334,15 @@ def main():
             torch.mul(cx, 1.0, out=cy)
         torch.cuda.synchronize()
         del cx, cy
+    cpu_inputs = None
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(spec, d, a.cpu_sample)
+        cpu_inputs = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in d.items()}
+    if not a.no_hbm_stages:
+        del d, w, out, ws
+        torch.cuda.empty_cache()
+        line.update(hbm_stages(torch, moe, dev))
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(spec, cpu_inputs, a.cpu_sample)
     print(json.dumps(line), flush=True)
 
 
