@@ -243,13 +243,17 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   // ---- tile decode (XCD-aware grouped order) ----
+  // split K: the grid holds ksplit copies of the tile grid, split-major
+  const int grid1 = static_cast<int>(gridDim.x) / p.ksplit;
+  const int ks = static_cast<int>(blockIdx.x) / grid1;
+  const int bid = static_cast<int>(blockIdx.x) - ks * grid1;
   const int rows_total = (C::AMODE == A_DENSE) ? p.T : p.ntp[0];
   const int n_mblk = (rows_total + BM - 1) / BM;
   const int total = n_mblk * p.n_tiles;
   const int per = (total + 7) >> 3;
-  const int jj = blockIdx.x >> 3;
+  const int jj = bid >> 3;
   if (jj >= per) return;
-  const int logical = (blockIdx.x & 7) * per + jj;
+  const int logical = (bid & 7) * per + jj;
   if (logical >= total) return;
   constexpr int GM = 8;
   const int grp = logical / (GM * p.n_tiles);
@@ -352,7 +356,11 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
     // made visible by the first k-tile's barrier
   }
 
+  // this workgroup's k-tiles: [kbase, kbase + nk)
+  const int nk = p.K / (RB / EB) / p.ksplit;
+  const int kbase = ks * nk;
   auto dma = [&](int kt, int buf) {
+    kt += kbase;
 #pragma unroll
     for (int s = 0; s < NIW; ++s) {
       const int j = wave + NW * s;
@@ -372,7 +380,6 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
 #pragma unroll
         for (int v = 0; v < NACC; ++v) acc[g][fm][fn][v] = 0.f;
 
-  const int nk = p.K / (RB / EB);
   const int row_w = wm * WM;
   // fragments of this wave that hold at least one data row (wave-uniform)
   const int fm_live = __builtin_amdgcn_readfirstlane(
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
     constexpr bool FULL = decltype(full_tag)::value;
     float rsa = 0.f;
     if constexpr (FP8) {
-      if (tid < BM) sA[tid] = p.a_scale[static_cast<int64_t>(a_srow) * kblocks];
+      if (tid < BM) sA[tid] = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kbase];
     }
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st)
@@ -404,7 +411,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
       lds_barrier();
       if (kt + NSTAGE - 1 < nk) {
         if constexpr (FP8)
-          if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kt + 1];
+          if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kbase + kt + 1];
         dma(kt + NSTAGE - 1, nbuf);
       }
       const uint8_t* As = smem + buf * STAGE;
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
           }
         }
       } else {
-        const float swg[2] = {sW[kt], C::GATED ? sW[kMaxKB + kt] : 0.f};
+        const float swg[2] = {sW[kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
         const float* sAb = sA + (kt & 1) * BM;
         // Every live fragment's k-tile partial: the NSUB substeps are issued
         // across all fragments before any promotion, so no MFMA waits on the
@@ -507,6 +514,27 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
   __syncthreads();
 
   // ---- epilogue ----
+  if (p.ksplit > 1) {
+    // fp32 partial tile; the reduction kernel applies the real epilogue
+    float* part = p.partial + static_cast<int64_t>(ks) * p.part_rows * p.ldp;
+    const int row_end = (C::AMODE == A_DENSE) ? min(BM, p.T - m0) : valid_rows;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int v = 0; v < NACC; ++v) {
+            const int r = row_w + fm * MF + acc_row<MF>(v, lane);
+            if (r < row_end) {
+              const int cc = wn * WN + fn * MF + acc_col<MF>(lane);
+              part[static_cast<int64_t>(m0 + r) * p.ldp + g * p.inter + n0 + cc] =
+                  acc[g][fm][fn][v];
+            }
+          }
+    return;
+  }
   if constexpr (C::EPI == EPI_Z) {
     // z = silu(gate) * up (gated) or silu(h); staged in LDS, then written as
     // whole rows: bf16, or fp8 E4M3 G(128) along I with one scale per row.
@@ -599,7 +627,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
 template <class C>
 void launch_gemm(const GemmParams& p, int64_t max_mblk, hipStream_t s) {
   const int64_t tiles = max_mblk * p.n_tiles;
-  const int64_t grid = (tiles + 7) / 8 * 8;
+  const int64_t grid = (tiles + 7) / 8 * 8 * p.ksplit;
   if (grid == 0) return;
   grouped_gemm_kernel<C><<<static_cast<unsigned>(grid), 64 * C::WAVES_M * C::WAVES_N, 0, s>>>(p);
 }

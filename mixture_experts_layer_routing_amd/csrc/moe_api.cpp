@@ -97,10 +97,80 @@ int check_weights(const moe_weights* w, int H, int activation, bool need_ptrs) {
   return MOE_OK;
 }
 
+// Tile height of the routed second GEMM: z is read row-contiguously, so the
+// tile may be half an align block; 256-row bf16 blocks use 128-row tiles
+// (twice the workgroups over H).
+int second_gemm_bm(bool fp8, int bm) { return (!fp8 && bm == 256) ? 128 : bm; }
+
+// Split K (see GemmParams::ksplit): a launch with fewer than 384 output
+// tiles (1.5 per CU; decode-sized T, or the shared expert over a few
+// tokens) cuts its k-tiles into 2, 4 or 8 ranges.  S doubles while the grid
+// stays within 1024 workgroups, every range keeps at least 8 k-tiles, and
+// the fp32 partials (written and read once: 8*S*rows*ldp bytes) stay within
+// half the weight bytes the launch streams.  The routed tile count and the
+// touched experts are estimated from n = T*k alone (min(E, n) experts, each
+// starting a block, the other rows filling further blocks), since the real
+// ones are known only on the device.
+int pick_ksplit(int64_t tiles, int K, int ktile, int64_t rows, int64_t ldp, double wbytes) {
+  if (tiles >= 384) return 1;
+  const int nk = K / ktile;
+  int S = 1;
+  while (S < 8 && tiles * S * 2 <= 1024 && nk % (2 * S) == 0 && nk / (2 * S) >= 8 &&
+         8.0 * (2 * S) * rows * ldp <= 0.5 * wbytes)
+    S *= 2;
+  return S;
+}
+
+struct SplitPlan {
+  int s1, s2, s3, s4;   // routed GEMM-1, routed GEMM-2, shared GEMM-1, shared GEMM-2
+  size_t partial_bytes;
+};
+
+SplitPlan split_plan(int T, int H, int top_k, const moe_weights* w, int activation, int bm) {
+  using namespace moe;
+  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const bool gated = activation == MOE_ACT_SILU_MUL;
+  const int ktile = fp8 ? 128 : 64;
+  const int E = w->num_experts, I = w->inter;
+  const int64_t n = static_cast<int64_t>(T) * top_k;
+  const double eb = fp8 ? 1.0 : 2.0;
+  const int64_t touched = std::min<int64_t>(E, n);
+  auto est_blocks = [&](int b) { return touched + (n - touched) / b; };
+  SplitPlan sp{1, 1, 1, 1, 0};
+  const int64_t rows = capacities(T, top_k, E, bm).block_cap * bm;
+  const int64_t R = gated ? 2 * I : I;
+  const int bn1 = gemm_tile_n(GEMM_Z_ROUTED, fp8, gated, bm, I);
+  sp.s1 = pick_ksplit(est_blocks(bm) * (I / bn1), H, ktile, rows, R,
+                      static_cast<double>(touched) * R * H * eb);
+  const int bm2 = second_gemm_bm(fp8, bm);
+  const int bn2 = gemm_tile_n(GEMM_Y_ROUTED, fp8, gated, bm2, H);
+  sp.s2 = pick_ksplit(est_blocks(bm2) * (H / bn2), I, ktile, rows, H,
+                      static_cast<double>(touched) * H * I * eb);
+  size_t b = 0;
+  if (sp.s1 > 1) b = std::max<size_t>(b, static_cast<size_t>(sp.s1) * rows * R * 4);
+  if (sp.s2 > 1) b = std::max<size_t>(b, static_cast<size_t>(sp.s2) * rows * H * 4);
+  if (w->shared_inter > 0) {
+    const int Is = w->shared_inter;
+    const int dbm = dense_block_m(T);
+    const int64_t mblk = (T + dbm - 1) / dbm;
+    const int64_t Rs = gated ? 2 * Is : Is;
+    const int bn3 = gemm_tile_n(GEMM_Z_DENSE, fp8, gated, dbm, Is);
+    sp.s3 = pick_ksplit(mblk * (Is / bn3), H, ktile, T, Rs, static_cast<double>(Rs) * H * eb);
+    const int bn4 = gemm_tile_n(GEMM_Y_DENSE, fp8, gated, dbm, H);
+    sp.s4 = pick_ksplit(mblk * (H / bn4), Is, ktile, T, H, static_cast<double>(H) * Is * eb);
+    if (sp.s3 > 1) b = std::max<size_t>(b, static_cast<size_t>(sp.s3) * T * Rs * 4);
+    if (sp.s4 > 1) b = std::max<size_t>(b, static_cast<size_t>(sp.s4) * T * H * 4);
+  }
+  sp.partial_bytes = b;
+  return sp;
+}
+
 // Workspace of the experts stage: z for the routed rows and for the shared
-// expert, in the GEMM input format of the second GEMM.
-size_t experts_ws(int T, int top_k, const moe_weights* w, int bm, Carve& c, void** z,
-                  float** zs, void** zsh, float** zshs, size_t* offs = nullptr) {
+// expert, in the GEMM input format of the second GEMM, then the split-K
+// partial sums (shared by the launches, which run in stream order).
+size_t experts_ws(int T, int H, int top_k, const moe_weights* w, int activation, int bm,
+                  Carve& c, void** z, float** zs, void** zsh, float** zshs, float** part,
+                  size_t* offs = nullptr) {
   const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
   const size_t eb = fp8 ? 1 : 2;
   const Caps cp = capacities(T, top_k, w->num_experts, bm);
@@ -125,6 +195,8 @@ size_t experts_ws(int T, int top_k, const moe_weights* w, int bm, Carve& c, void
       o[3] = c.last - start;
     }
   }
+  const SplitPlan sp = split_plan(T, H, top_k, w, activation, bm);
+  *part = sp.partial_bytes ? static_cast<float*>(c.take(sp.partial_bytes)) : nullptr;
   if (offs) for (int i = 0; i < 5; ++i) offs[i] = o[i];
   return c.used - start;
 }
@@ -150,12 +222,21 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   const int R = gated ? 2 * I : I;
   Carve c(ws);
   void *z, *zsh;
-  float *zs, *zshs;
-  experts_ws(T, top_k, w, bm, c, &z, &zs, &zsh, &zshs);
+  float *zs, *zshs, *part;
+  experts_ws(T, H, top_k, w, activation, bm, c, &z, &zs, &zsh, &zshs, &part);
+  const SplitPlan sp = split_plan(T, H, top_k, w, activation, bm);
   const Caps cp = capacities(T, top_k, E, bm);
+  const int64_t rows = cp.block_cap * bm;
+  const int nflat = T * top_k;
   auto launch = [&](int kind, int blk_m, int bnz, const GemmParams& p, int64_t max_mblk) {
     if (fp8) launch_gemm_fp8(kind, gated, blk_m, bnz, p, max_mblk, s);
     else launch_gemm_bf16(kind, gated, blk_m, bnz, p, max_mblk, s);
+  };
+  auto split = [&](GemmParams& g, int S, int64_t part_rows, int ldp) {
+    g.ksplit = S;
+    g.partial = S > 1 ? part : nullptr;
+    g.part_rows = part_rows;
+    g.ldp = ldp;
   };
   // routed first GEMM: gather a1q rows, activation, z [rows, I]
   GemmParams p{};
@@ -178,12 +259,13 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   p.out = z;
   p.out_scale = zs;
   p.ldo = I;
+  split(p, sp.s1, rows, R);
   launch(GEMM_Z_ROUTED, bm, bn1, p, cp.block_cap);
+  if (sp.s1 > 1)
+    launch_splitk_z(part, sp.s1, rows, R, rows, ntp, sorted, nflat, T, I, gated, fp8, z, zs, I, s);
   se.mark(4);
-  // routed second GEMM: z rows -> fused_expert_output[sorted row].  z is
-  // read row-contiguously, so the tile may be half an align block: 256-row
-  // blocks use 128-row tiles here (twice the workgroups over H).
-  const int bm2 = (!fp8 && bm == 256) ? 128 : bm;
+  // routed second GEMM: z rows -> fused_expert_output[sorted row]
+  const int bm2 = second_gemm_bm(fp8, bm);
   GemmParams q{};
   q.a = static_cast<const uint8_t*>(z);
   q.a_scale = zs;
@@ -203,7 +285,9 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   q.align_bm = bm;
   q.out = feo;
   q.ldo = H;
+  split(q, sp.s2, rows, H);
   launch(GEMM_Y_ROUTED, bm2, bn2, q, cp.block_cap * (bm / bm2));
+  if (sp.s2 > 1) launch_splitk_y(part, sp.s2, rows, H, rows, ntp, sorted, nflat, T, H, feo, H, s);
   se.mark(5);
   if (w->shared_inter > 0) {
     const int Is = w->shared_inter;
@@ -225,8 +309,11 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
     d.out = zsh;
     d.out_scale = zshs;
     d.ldo = Is;
-    (void)Rs;
+    split(d, sp.s3, T, Rs);
     launch(GEMM_Z_DENSE, dbm, bn3, d, mblk);
+    if (sp.s3 > 1)
+      launch_splitk_z(part, sp.s3, T, Rs, T, nullptr, nullptr, 0, T, Is, gated, fp8, zsh, zshs, Is,
+                      s);
     GemmParams e{};
     e.a = static_cast<const uint8_t*>(zsh);
     e.a_scale = zshs;
@@ -240,7 +327,10 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
     e.align_bm = dbm;
     e.out = shared_out;
     e.ldo = H;
+    split(e, sp.s4, T, H);
     launch(GEMM_Y_DENSE, dbm, bn4, e, mblk);
+    if (sp.s4 > 1)
+      launch_splitk_y(part, sp.s4, T, H, T, nullptr, nullptr, 0, T, H, shared_out, H, s);
   }
   se.mark(6);
   return check_launch("moe_experts");
@@ -359,8 +449,8 @@ size_t moe_experts_workspace_bytes(int T, int H, int top_k, const moe_weights* w
   if (check_weights(weights, H, activation, false) != MOE_OK) return 0;
   Carve c(nullptr);
   void *z, *zsh;
-  float *zs, *zshs;
-  return experts_ws(T, top_k, weights, block_m, c, &z, &zs, &zsh, &zshs);
+  float *zs, *zshs, *part;
+  return experts_ws(T, H, top_k, weights, activation, block_m, c, &z, &zs, &zsh, &zshs, &part);
 }
 
 int moe_experts_workspace_layout(int T, int H, int top_k, const moe_weights* weights,
@@ -371,8 +461,8 @@ int moe_experts_workspace_layout(int T, int H, int top_k, const moe_weights* wei
   if (int st = check_weights(weights, H, activation, false)) return st;
   Carve c(nullptr);
   void *z, *zsh;
-  float *zs, *zshs;
-  experts_ws(T, top_k, weights, block_m, c, &z, &zs, &zsh, &zshs, out);
+  float *zs, *zshs, *part;
+  experts_ws(T, H, top_k, weights, activation, block_m, c, &z, &zs, &zsh, &zshs, &part, out);
   return MOE_OK;
 }
 
@@ -447,8 +537,8 @@ struct ForwardLayout {
   uint16_t* shared_out;
 };
 
-size_t forward_layout(int T, int H, int top_k, const moe_weights* w, int bm, int woi,
-                      void* base, ForwardLayout* L) {
+size_t forward_layout(int T, int H, int top_k, const moe_weights* w, int activation, int bm,
+                      int woi, void* base, ForwardLayout* L) {
   Carve c(base);
   const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
   const size_t eb = fp8 ? 1 : 2;
@@ -473,8 +563,8 @@ size_t forward_layout(int T, int H, int top_k, const moe_weights* w, int bm, int
   L->align_ws = c.take(moe::align_workspace_bytes(n, E));
   Carve sub(nullptr);
   void *z, *zsh;
-  float *zs, *zshs;
-  L->experts_ws_bytes = experts_ws(T, top_k, w, bm, sub, &z, &zs, &zsh, &zshs);
+  float *zs, *zshs, *part;
+  L->experts_ws_bytes = experts_ws(T, H, top_k, w, activation, bm, sub, &z, &zs, &zsh, &zshs, &part);
   L->experts_ws = c.take(L->experts_ws_bytes);
   L->feo = static_cast<uint16_t*>(c.take(static_cast<size_t>(n) * H * 2));
   L->shared_out = w->shared_inter > 0 ? static_cast<uint16_t*>(c.take(static_cast<size_t>(T) * H * 2))
@@ -491,7 +581,8 @@ size_t moe_forward_workspace_bytes(int T, int H, int top_k, const moe_weights* w
   const int bm = block_m ? block_m : moe_pick_block_m(T, top_k, weights->num_experts, weights->quant);
   if (!valid_block_m(bm)) return 0;
   ForwardLayout L;
-  return forward_layout(T, H, top_k, weights, bm, apply_router_weight_on_input, nullptr, &L);
+  return forward_layout(T, H, top_k, weights, activation, bm, apply_router_weight_on_input, nullptr,
+                        &L);
 }
 
 int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k, int scoring,
@@ -522,11 +613,12 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
   if (!x || !logits || !output || (out_quant == MOE_QUANT_FP8_G128 && !output_scale))
     return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
   ForwardLayout L;
-  const size_t need = forward_layout(T, H, top_k, weights, bm, apply_router_weight_on_input,
-                                     nullptr, &L);
+  const size_t need = forward_layout(T, H, top_k, weights, activation, bm,
+                                     apply_router_weight_on_input, nullptr, &L);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "forward workspace %zu < %zu", workspace_bytes, need);
-  forward_layout(T, H, top_k, weights, bm, apply_router_weight_on_input, workspace, &L);
+  forward_layout(T, H, top_k, weights, activation, bm, apply_router_weight_on_input, workspace,
+                 &L);
   const StageEvents se{stage_events, stream};
   const int quant = weights->quant;
   const int64_t n = static_cast<int64_t>(T) * top_k;

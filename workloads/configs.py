@@ -95,4 +95,13 @@ PARITY_CASES = [
                  shared_I=256, residual=True, rmsnorm=True),
     WorkloadSpec("fp8_out_mini", 3, T=77, H=512, I=256, E=16, top_k=4, scoring="sigmoid",
                  quant="fp8", residual=True, rmsnorm=True, out_quant="fp8"),
+    # Decode-sized batches with K long enough that the GEMMs split K (a few
+    # expert blocks cannot fill the GPU): bf16 SiLU-mul with a shared expert,
+    # fp8, and top-1 weight-on-input silu_no_mul.
+    WorkloadSpec("decode_split_mini", 6, T=5, H=2048, I=2048, E=4, top_k=2, shared_I=2048),
+    WorkloadSpec("decode_split_fp8_mini", 7, T=3, H=2048, I=2048, E=16, top_k=4,
+                 scoring="sigmoid", quant="fp8", shared_I=1024),
+    WorkloadSpec("decode_split_no_mul_mini", 8, T=4, H=2048, I=2048, E=16, top_k=1,
+                 renormalize=False, apply_router_weight_on_input=True, shared_I=2048,
+                 activation="silu_no_mul"),
 ]
