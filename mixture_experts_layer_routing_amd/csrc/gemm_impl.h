@@ -231,8 +231,9 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
   static_assert(NSTAGE == 2 || (!FP8 && NI % NW == 0), "deeper pipelines: bf16, whole load groups");
   constexpr int SMEM_TILE = cmax(NSTAGE * STAGE, EPI_BYTES);
   // fp8 only, after the stages: the activation scales of two k-tiles
-  // (sA) and the tile's weight-block scales along K (sW: gate row, then up
-  // row).  bf16 tiles use every byte of the 160 KB for stages.
+  // (sA: this one and the next) and the tile's weight-block scales along K
+  // (sW: gate row, then up row).  bf16 tiles use every byte of the 160 KB
+  // for stages.
   constexpr int kMaxKB = 128;  // K <= 16384
   constexpr int SCALE_BYTES = FP8 ? (2 * BM + 2 * kMaxKB) * 4 : 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_TILE + SCALE_BYTES];
@@ -385,14 +386,91 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
   const int fm_live = __builtin_amdgcn_readfirstlane(
       valid_rows > row_w ? min(FM, (valid_rows - row_w + MF - 1) / MF) : 0);
 
+  // fp8 k-loop.  A k-tile is one 128-deep scale block: its MFMAs sum into a
+  // fresh partial, which is promoted into the fp32 accumulator as
+  // acc += partial * s_a[row] * s_w.  The k-tile's activation scales are
+  // read from LDS (16-byte reads: an accumulator's rows come in runs of 4)
+  // right after the barrier, so their latency hides behind the MFMAs.
+  // (Deferring each promotion by one k-tile with two partial sets was
+  // measured slower: the extra registers cost occupancy.)
+  auto kloop_fp8 = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    static_assert(!FP8 || NSTAGE == 2, "fp8 runs two LDS stages");
+    if (tid < BM) sA[tid] = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kbase];
+    if (nk > 0) dma(0, 0);
+    int buf = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vm_loads();
+      lds_barrier();
+      float rsa = 0.f;
+      if (kt + 1 < nk) {
+        if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kbase + kt + 1];
+        dma(kt + 1, buf ^ 1);
+      }
+      // this k-tile's scales: weight blocks (gate, up) and the rows' activation scales
+      const float swg[2] = {sW[kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
+      const float* sAb = sA + (kt & 1) * BM;
+      float sa[FM][NACC];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int q = 0; q < NACC / 4; ++q) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(sAb + row_w + fm * MF + acc_row<MF>(4 * q, lane));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sa[fm][4 * q + r] = t[r];
+        }
+      const uint8_t* As = smem + buf * STAGE;
+      const uint8_t* Bs = As + A_BYTES;
+      acc_t part[G][FM][FN];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        frag_t fa[FM], fb[G][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          if (FULL || fm < fm_live) fa[fm] = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            fb[g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          if (FULL || fm < fm_live)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+              for (int fn = 0; fn < FN; ++fn) {
+                if (s == 0) {
+#pragma unroll
+                  for (int v = 0; v < NACC; ++v) part[g][fm][fn][v] = 0.f;
+                }
+                part[g][fm][fn] = M::mma(fa[fm], fb[g][fn], part[g][fm][fn]);
+              }
+      }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        if (!(FULL || fm < fm_live)) continue;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int v = 0; v < NACC; ++v)
+              acc[g][fm][fn][v] += part[g][fm][fn][v] * (sa[fm][v] * swg[g]);
+      }
+      if (kt + 1 < nk && tid < BM) sA[((kt + 1) & 1) * BM + tid] = rsa;
+      buf ^= 1;
+    }
+  };
+
   // The k-loop, instantiated twice: branch-free when every fragment row
   // block holds data (all but an expert's last block), and with uniform
   // per-fragment guards otherwise.
   auto kloop = [&](auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    float rsa = 0.f;
     if constexpr (FP8) {
-      if (tid < BM) sA[tid] = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kbase];
+      kloop_fp8(full_tag);
+      return;
     }
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st)
@@ -409,14 +487,10 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
         wait_vm_loads();
       }
       lds_barrier();
-      if (kt + NSTAGE - 1 < nk) {
-        if constexpr (FP8)
-          if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kbase + kt + 1];
-        dma(kt + NSTAGE - 1, nbuf);
-      }
+      if (kt + NSTAGE - 1 < nk) dma(kt + NSTAGE - 1, nbuf);
       const uint8_t* As = smem + buf * STAGE;
       const uint8_t* Bs = As + A_BYTES;
-      if constexpr (!FP8) {
+      {
         // Two fragment sets: substep s+1's LDS reads are in flight while
         // substep s's MFMAs issue (interleaved by sched_group_barrier).
         frag_t fa[2][FM], fb[2][G][FN];
@@ -457,53 +531,6 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
             }
           }
         }
-      } else {
-        const float swg[2] = {sW[kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
-        const float* sAb = sA + (kt & 1) * BM;
-        // Every live fragment's k-tile partial: the NSUB substeps are issued
-        // across all fragments before any promotion, so no MFMA waits on the
-        // previous one's result.
-        acc_t part[G][FM][FN];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          frag_t fa[FM], fb[G][FN];
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-            if (FULL || fm < fm_live) fa[fm] = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-              fb[g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-            if (FULL || fm < fm_live)
-#pragma unroll
-              for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                  if (s == 0) {
-#pragma unroll
-                    for (int v = 0; v < NACC; ++v) part[g][fm][fn][v] = 0.f;
-                  }
-                  part[g][fm][fn] = M::mma(fa[fm], fb[g][fn], part[g][fm][fn]);
-                }
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          if (!(FULL || fm < fm_live)) continue;
-          float sa[NACC];
-#pragma unroll
-          for (int v = 0; v < NACC; ++v) sa[v] = sAb[row_w + fm * MF + acc_row<MF>(v, lane)];
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-              for (int v = 0; v < NACC; ++v)
-                acc[g][fm][fn][v] += part[g][fm][fn][v] * (sa[v] * swg[g]);
-        }
-        if (kt + 1 < nk && tid < BM) sA[(kt + 1 & 1) * BM + tid] = rsa;
       }
       buf = buf + 1 == NSTAGE ? 0 : buf + 1;
       nbuf = nbuf + 1 == NSTAGE ? 0 : nbuf + 1;
