@@ -146,9 +146,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(
           u32x2 q;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) word |= f32_to_e4m3(o[4 * h + v] / s) << (8 * v);
+            const uint32_t word = pack4_e4m3(o[4 * h] / s, o[4 * h + 1] / s, o[4 * h + 2] / s,
+                                   o[4 * h + 3] / s);
             q[h] = word;
           }
           __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(static_cast<uint8_t*>(output) + row + c * 8));

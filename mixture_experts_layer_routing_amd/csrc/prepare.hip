@@ -66,9 +66,8 @@ __global__ __launch_bounds__(256) void prepare_fp8_kernel(
   u32x2 o;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) word |= f32_to_e4m3(f[4 * h + i] / s) << (8 * i);
+    const uint32_t word = pack4_e4m3(f[4 * h] / s, f[4 * h + 1] / s, f[4 * h + 2] / s,
+                                   f[4 * h + 3] / s);
     o[h] = word;
   }
   if (valid) {

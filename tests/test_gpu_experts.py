@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import CONFIGS, PARITY_CASES, make_layer_inputs, to_numpy_bits
+from workloads import WorkloadSpec, CONFIGS, PARITY_CASES, make_layer_inputs, to_numpy_bits
 from helpers import (check_tolerance, check_fp8_codes, f64_of_bf16, f64_of_fp8,
                      finalize_flip_allowance)
 
@@ -218,6 +218,43 @@ def test_forward_unit_weight_on_input_matches_no_flag():
     b, _, _ = moe.moe_forward(d["x"], d["logits"], w, 1, "softmax", True, False)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+DEGENERATE = [
+    # one expert, top-1: the layer is a dense SwiGLU MLP (router weight 1)
+    WorkloadSpec("single_expert", 11, T=37, H=256, I=128, E=1, top_k=1),
+    # top_k = E: every token visits every expert
+    WorkloadSpec("all_experts", 12, T=29, H=256, I=128, E=4, top_k=4),
+    # the largest hidden size the library accepts (GEMM-1 K = 16384)
+    WorkloadSpec("max_hidden", 13, T=3, H=16384, I=64, E=2, top_k=1, renormalize=False),
+    # the largest fp8 intermediate (GEMM-2 K = 16384: 128 weight-scale blocks along K)
+    WorkloadSpec("max_inter_fp8", 14, T=2, H=256, I=16384, E=2, top_k=2, quant="fp8"),
+    # the largest expert count
+    WorkloadSpec("max_experts", 15, T=9, H=256, I=128, E=1024, top_k=4, scoring="sigmoid"),
+]
+
+
+@pytest.mark.parametrize("spec", DEGENERATE, ids=lambda s: s.name)
+def test_forward_degenerate_and_limit_shapes(spec):
+    _announce(f"forward limits {spec.name}")
+    moe = _moe()
+    d = make_layer_inputs(spec)
+    dd = {k: v.to(DEV) for k, v in d.items()}
+    w = _weights(moe, dd)
+    hw = _host_w(d)
+    refs = {mode: oracle.forward(to_numpy_bits(d["x"]), d["logits"].numpy(), hw, spec.top_k,
+                                 spec.scoring, spec.renormalize, 16,
+                                 spec.apply_router_weight_on_input, spec.quant, spec.activation,
+                                 mode)
+            for mode in ("exact", "mirrored")}
+    out, scale, _ = moe.moe_forward(dd["x"], dd["logits"], w, spec.top_k, spec.scoring,
+                                    spec.renormalize, spec.apply_router_weight_on_input,
+                                    spec.activation)
+    torch.cuda.synchronize()
+    check_tolerance(_out_f64(spec, out, scale), _ref_f64(spec, refs["exact"]),
+                    _ref_f64(spec, refs["mirrored"]), _path(spec), spec.name,
+                    elementwise=spec.quant != "fp8",
+                    allowance=finalize_flip_allowance(refs["mirrored"]))
 
 
 # ------------------------------------------------ full sizes, sampled tokens
