@@ -199,8 +199,17 @@ __device__ __forceinline__ void wait_vm_loads_but() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Occupancy hint: the fp8 second-GEMM tile of 128 rows (64 KB of LDS) is
+// held to 128 VGPRs so that two workgroups share a CU, one's prologue and
+// epilogue overlapping the other's k-loop (its k-loop is only K/128 = 16
+// tiles long at the DeepSeek shape, so those fixed costs weigh ~20 %).
 template <class C>
-__global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_kernel(GemmParams p) {
+constexpr int gemm_min_waves_per_eu() {
+  return (C::FP8 && C::EPI != EPI_Z && C::BM == 128) ? 4 : 1;
+}
+
+template <class C>
+__global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu<C>()) void grouped_gemm_kernel(GemmParams p) {
   constexpr int BM = C::BM, BNZ = C::BNZ, MF = C::MF;
   constexpr bool FP8 = C::FP8;
   constexpr int G = C::GATED ? 2 : 1;
@@ -407,18 +416,25 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
         if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kbase + kt + 1];
         dma(kt + 1, buf ^ 1);
       }
-      // this k-tile's scales: weight blocks (gate, up) and the rows' activation scales
+      // this k-tile's scales: weight blocks (gate, up) and the rows' activation
+      // scales; the latter are read ahead of the MFMAs unless registers are
+      // held to 128 for occupancy (LEAN), then inside the promotion
+      constexpr bool LEAN = gemm_min_waves_per_eu<C>() > 1;
       const float swg[2] = {sW[kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
       const float* sAb = sA + (kt & 1) * BM;
-      float sa[FM][NACC];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      auto read_sa = [&](int fm, float (&out)[NACC]) {
 #pragma unroll
         for (int q = 0; q < NACC / 4; ++q) {
           const f32x4 t = *reinterpret_cast<const f32x4*>(sAb + row_w + fm * MF + acc_row<MF>(4 * q, lane));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sa[fm][4 * q + r] = t[r];
+          for (int r = 0; r < 4; ++r) out[4 * q + r] = t[r];
         }
+      };
+      float sa[LEAN ? 1 : FM][NACC];
+      if constexpr (!LEAN) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) read_sa(fm, sa[fm]);
+      }
       const uint8_t* As = smem + buf * STAGE;
       const uint8_t* Bs = As + A_BYTES;
       acc_t part[G][FM][FN];
@@ -450,13 +466,21 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N) void grouped_gemm_ker
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         if (!(FULL || fm < fm_live)) continue;
+        const float* sr = sa[0];
+        float lean[NACC];
+        if constexpr (LEAN) {
+          read_sa(fm, lean);
+          sr = lean;
+        } else {
+          sr = sa[fm];
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
             for (int v = 0; v < NACC; ++v)
-              acc[g][fm][fn][v] += part[g][fm][fn][v] * (sa[fm][v] * swg[g]);
+              acc[g][fm][fn][v] += part[g][fm][fn][v] * (sr[v] * swg[g]);
       }
       if (kt + 1 < nk && tid < BM) sA[((kt + 1) & 1) * BM + tid] = rsa;
       buf ^= 1;
