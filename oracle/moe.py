@@ -19,6 +19,10 @@ table of the design notes lists them all):
     128x128 block of each matrix;
   * SiLU-mul: z = silu(gate) * up with silu(v) = v / (1 + exp(-v));
     silu_no_mul: z = silu(W1 a) with W13 holding only the I gate rows;
+  * gelu / gelu_no_mul (the activation column of the fused-experts kernel
+    table, which lists gelu_tanh separately): the exact GELU
+    gelu(v) = v * Phi(v) = v/2 * (1 + erf(v / sqrt 2)), gated and ungated
+    like silu;
   * the shared expert runs the same MLP on every token's unweighted input
     and is added with weight 1 in finalize.
 """
@@ -192,6 +196,17 @@ def silu(v):
     return v / (1.0 + np.exp(-v))
 
 
+def gelu(v):
+    """Exact GELU, v * Phi(v), with the standard normal CDF Phi written
+    through erf (scipy's double-precision erf as the library primitive)."""
+    from scipy.special import erf
+    v = np.asarray(v, np.float64)
+    return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+
+
+_ACTS = {"silu": silu, "gelu": gelu}
+
+
 def dequant_weight(w, scale):
     """One expert matrix [N, K] -> float64.  bf16 bits when ``scale`` is
     None, else E4M3 codes times one float32 scale per 128x128 block."""
@@ -230,11 +245,11 @@ def expert_gemm1(a, w13, activation="silu"):
     h = a @ w13.T
     if callable(activation):        # a test-only activation without a gate/up split
         return activation(h)
-    if activation == "silu":
+    if activation in ("silu", "gelu"):
         inter = w13.shape[0] // 2
-        return silu(h[:, :inter]) * h[:, inter:]
-    if activation == "silu_no_mul":
-        return silu(h)
+        return _ACTS[activation](h[:, :inter]) * h[:, inter:]
+    if activation in ("silu_no_mul", "gelu_no_mul"):
+        return _ACTS[activation[:-len("_no_mul")]](h)
     raise ValueError(activation)
 
 

@@ -52,6 +52,49 @@ def test_silu_no_mul_is_silu_then_down_projection():
     np.testing.assert_array_equal(feo[:, 0], _bf16_bits(ref.numpy()))
 
 
+def test_gelu_closed_forms():
+    """GELU(v) = v * Phi(v): the textbook value Phi(1) = 0.8413447460685429,
+    GELU(v) - GELU(-v) = v (Phi(v) + Phi(-v) = 1), GELU(0) = 0, and
+    GELU(v) -> v for large v."""
+    g = oracle.moe.gelu
+    assert g(0.0) == 0.0
+    assert abs(g(1.0) - 0.8413447460685429) < 1e-15
+    assert abs(g(-1.0) + 0.15865525393145707) < 1e-15
+    v = np.linspace(-6, 6, 97)
+    np.testing.assert_allclose(g(v) - g(-v), v, rtol=0, atol=1e-14)
+    assert abs(g(10.0) - 10.0) < 1e-20
+
+
+def test_gelu_mul_single_expert_matches_torch_exact_gelu():
+    """E = 1, k = 1 with the gated GELU: y = W2 (gelu(W1 x) * (W3 x)), with
+    torch's erf-form GELU in float64 (not the tanh approximation)."""
+    rng = np.random.default_rng(24)
+    T, H, I = 9, 48, 20
+    x = _rand_bf16(rng, (T, H))
+    w13 = _rand_bf16(rng, (1, 2 * I, H), 0.3)
+    w2 = _rand_bf16(rng, (1, H, I), 0.3)
+    feo, _ = oracle.experts(x, None, np.zeros((T, 1), np.int32), w13, None, w2, None, "gelu",
+                            "exact")
+    xt, W13, W2 = _f64(x), _f64(w13[0]), _f64(w2[0])
+    ref = (F.gelu(xt @ W13[:I].T, approximate="none") * (xt @ W13[I:].T)) @ W2.T
+    np.testing.assert_array_equal(feo[:, 0], _bf16_bits(ref.numpy()))
+    # and not the tanh form, which differs by more than bf16 rounding here
+    tanh = (F.gelu(xt @ W13[:I].T, approximate="tanh") * (xt @ W13[I:].T)) @ W2.T
+    assert not np.array_equal(_bf16_bits(tanh.numpy()), feo[:, 0])
+
+
+def test_gelu_no_mul_is_gelu_then_down_projection():
+    rng = np.random.default_rng(25)
+    T, H, I = 7, 40, 24
+    x = _rand_bf16(rng, (T, H))
+    w1 = _rand_bf16(rng, (1, I, H), 0.3)
+    w2 = _rand_bf16(rng, (1, H, I), 0.3)
+    feo, _ = oracle.experts(x, None, np.zeros((T, 1), np.int32), w1, None, w2, None,
+                            "gelu_no_mul", "exact")
+    ref = F.gelu(_f64(x) @ _f64(w1[0]).T) @ _f64(w2[0]).T
+    np.testing.assert_array_equal(feo[:, 0], _bf16_bits(ref.numpy()))
+
+
 def test_experts_match_dense_all_experts_then_mask():
     """Brute force: every expert on every token (one einsum over all experts),
     then pick each (token, slot) by topk_ids."""

@@ -23,7 +23,7 @@ class WorkloadSpec:
     scoring: str = "softmax"    # "softmax" | "sigmoid"
     renormalize: bool = True
     quant: str = "none"         # "none" | "fp8" (G(128) acts, 128x128 weight blocks)
-    activation: str = "silu"    # "silu" (SiLU-mul) | "silu_no_mul"
+    activation: str = "silu"    # "silu" (SiLU-mul) | "silu_no_mul" | "gelu" | "gelu_no_mul"
     apply_router_weight_on_input: bool = False
     shared_I: int = 0           # 0 = no shared expert
     logit_std: float = 1.0
@@ -104,4 +104,11 @@ PARITY_CASES = [
     WorkloadSpec("decode_split_no_mul_mini", 8, T=4, H=2048, I=2048, E=16, top_k=1,
                  renormalize=False, apply_router_weight_on_input=True, shared_I=2048,
                  activation="silu_no_mul"),
+    # the GELU activations of the fused-experts table: gated bf16 with a
+    # shared expert, ungated fp8 top-1 with the weight on the input
+    WorkloadSpec("gelu_mini", 9, T=131, H=384, I=256, E=8, top_k=2, shared_I=256,
+                 activation="gelu"),
+    WorkloadSpec("gelu_no_mul_fp8_mini", 10, T=93, H=512, I=256, E=16, top_k=1,
+                 renormalize=False, apply_router_weight_on_input=True, quant="fp8",
+                 activation="gelu_no_mul"),
 ]

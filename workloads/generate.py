@@ -54,8 +54,8 @@ def hot_expert_tokens(spec: WorkloadSpec, device="cpu"):
 
 def make_layer_inputs(spec: WorkloadSpec, device="cpu", weights=True):
     """All inputs of one layer call, as torch tensors on ``device``:
-    x bf16 [T,H]; logits f32 [T,E]; w13 [E,R,H] (R = 2I for SiLU-mul, I for
-    silu_no_mul) and w2 [E,H,I], bf16 or fp8 codes (uint8) with float32
+    x bf16 [T,H]; logits f32 [T,E]; w13 [E,R,H] (R = 2I for the gated
+    activations silu and gelu, I for silu_no_mul and gelu_no_mul) and w2 [E,H,I], bf16 or fp8 codes (uint8) with float32
     128x128 block scales w13_scale/w2_scale; optional shared_w13/shared_w2
     (+scales); optional residual bf16 [T,H] and gamma bf16 [H]."""
     base = 1000 * spec.config
@@ -72,10 +72,10 @@ def make_layer_inputs(spec: WorkloadSpec, device="cpu", weights=True):
     g = _gen(base + 2, device)
     out["x"] = _randn((T, H), g, device).to(torch.bfloat16)
     if weights:
-        R = 2 * I if spec.activation == "silu" else I
+        R = I if spec.activation.endswith("_no_mul") else 2 * I
         mats = [("w13", 3, E, R, H, H), ("w2", 4, E, H, I, I)]
         if spec.shared_I:
-            Rs = 2 * spec.shared_I if spec.activation == "silu" else spec.shared_I
+            Rs = spec.shared_I if spec.activation.endswith("_no_mul") else 2 * spec.shared_I
             mats += [("shared_w13", 5, 1, Rs, H, H), ("shared_w2", 6, 1, H, spec.shared_I, spec.shared_I)]
         for name, idx, n, rows, cols, fan_in in mats:
             g = _gen(base + idx, device)
