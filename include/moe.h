@@ -68,9 +68,15 @@ typedef enum moe_quant {
                                128x128 block of each matrix */
 } moe_quant;
 
+/* The activation names of the fused-experts kernel table ("Fused MoE Kernel
+ * Features", fused experts section): "silu", "silu_no_mul", "gelu",
+ * "gelu_no_mul".  gelu is the exact form v * Phi(v) = v/2 (1 + erf(v/sqrt 2))
+ * (the table lists the tanh approximation separately, as gelu_tanh). */
 typedef enum moe_activation {
   MOE_ACT_SILU_MUL = 0,     /* z = silu(gate) * up, silu(v) = v / (1 + exp(-v)) ("silu") */
-  MOE_ACT_SILU_NO_MUL = 1   /* z = silu(W1 a), no up projection ("silu_no_mul") */
+  MOE_ACT_SILU_NO_MUL = 1,  /* z = silu(W1 a), no up projection ("silu_no_mul") */
+  MOE_ACT_GELU_MUL = 2,     /* z = gelu(gate) * up ("gelu") */
+  MOE_ACT_GELU_NO_MUL = 3   /* z = gelu(W1 a), no up projection ("gelu_no_mul") */
 } moe_activation;
 
 /* Number of events moe_forward records when given a stage_events array. */
@@ -78,8 +84,9 @@ typedef enum moe_activation {
 
 /*
  * Expert weights (host struct holding device pointers).
- *   R = 2*inter for MOE_ACT_SILU_MUL (rows [0, I) = gate W1, rows [I, 2I) = up W3),
- *       inter   for MOE_ACT_SILU_NO_MUL (W1 only).
+ *   R = 2*inter for the gated activations MOE_ACT_SILU_MUL / MOE_ACT_GELU_MUL
+ *       (rows [0, I) = gate W1, rows [I, 2I) = up W3),
+ *       inter   for MOE_ACT_SILU_NO_MUL / MOE_ACT_GELU_NO_MUL (W1 only).
  *   w13        [E, R, H]   bf16 bits, or E4M3 codes (quant == MOE_QUANT_FP8_G128)
  *   w13_scale  [E, R/128, H/128] fp32 block scales (fp8 only, else NULL)
  *   w2         [E, H, I]

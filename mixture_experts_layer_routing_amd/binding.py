@@ -23,7 +23,7 @@ MOE_ERR_HIP = 4
 
 SCORING = {"softmax": 0, "sigmoid": 1}
 QUANT = {"none": 0, "fp8": 1}
-ACTIVATION = {"silu": 0, "silu_no_mul": 1}
+ACTIVATION = {"silu": 0, "silu_no_mul": 1, "gelu": 2, "gelu_no_mul": 3}
 NUM_STAGE_EVENTS = 8
 STAGES = ("start", "route", "prepare", "align", "gemm1", "gemm2", "shared", "finalize")
 

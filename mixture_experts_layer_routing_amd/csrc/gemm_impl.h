@@ -587,7 +587,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
     return;
   }
   if constexpr (C::EPI == EPI_Z) {
-    // z = silu(gate) * up (gated) or silu(h); staged in LDS, then written as
+    // z = act(gate) * up (gated) or act(h), act = SiLU or GELU; staged in LDS, then written as
     // whole rows: bf16, or fp8 E4M3 G(128) along I with one scale per row.
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
@@ -598,8 +598,8 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
           const int r = row_w + fm * MF + acc_row<MF>(v, lane);
           const int cc = wn * WN + fn * MF + acc_col<MF>(lane);
           float z;
-          if constexpr (C::GATED) z = silu_fast(acc[0][fm][fn][v]) * acc[G - 1][fm][fn][v];
-          else z = silu_fast(acc[0][fm][fn][v]);
+          if constexpr (C::GATED) z = act_apply(p.act, acc[0][fm][fn][v]) * acc[G - 1][fm][fn][v];
+          else z = act_apply(p.act, acc[0][fm][fn][v]);
           if constexpr (FP8) reinterpret_cast<float*>(smem)[r * BNZ + cc] = z;
           else reinterpret_cast<uint16_t*>(smem)[r * BNZ + cc] = static_cast<uint16_t>(f32_to_bf16_hw(z));
         }

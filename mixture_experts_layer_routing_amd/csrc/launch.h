@@ -43,6 +43,7 @@ struct GemmParams {
   void* out;               // z / fused_expert_output / shared_out
   float* out_scale;        // fp8 z scales [rows][ldo/128]
   int ldo;                 // output row length in elements
+  int act;                 // first GEMM's activation: ACT_SILU or ACT_GELU
   // Split K: ksplit > 1 cuts the k-tiles into ksplit equal ranges, one
   // workgroup each; every workgroup then writes its fp32 partial tile to
   // partial[split][row][col] (rows as in the output, part_rows per split,
@@ -54,13 +55,15 @@ struct GemmParams {
   int ldp;
 };
 
+enum ActFn { ACT_SILU = 0, ACT_GELU = 1 };
+
 // Finish a split first GEMM: z[r] = act(sum of partials) -> bf16 or fp8
 // G(128) (+ scales).  Rows: the padded routed rows up to *ntp (pad rows get
 // zeros), or the T dense rows when sorted == nullptr.
 void launch_splitk_z(const float* partial, int ksplit, int64_t part_rows, int ldp,
                      int64_t max_rows, const int32_t* ntp, const int32_t* sorted, int nflat,
-                     int T, int inter, bool gated, bool fp8, void* z, float* z_scale, int ldz,
-                     hipStream_t s);
+                     int T, int inter, bool gated, int act, bool fp8, void* z, float* z_scale,
+                     int ldz, hipStream_t s);
 // Finish a split second GEMM: y = bf16(sum of partials) written to
 // out[sorted[r]] (routed; pad rows skipped) or out[r] (dense rows < T).
 void launch_splitk_y(const float* partial, int ksplit, int64_t part_rows, int ldp,

@@ -47,6 +47,15 @@ struct Carve {
   }
 };
 
+// Gated activations read the gate and up halves of W13; GELU or SiLU.
+bool act_gated(int activation) {
+  return activation == MOE_ACT_SILU_MUL || activation == MOE_ACT_GELU_MUL;
+}
+int act_fn(int activation) {
+  return (activation == MOE_ACT_GELU_MUL || activation == MOE_ACT_GELU_NO_MUL) ? moe::ACT_GELU
+                                                                               : moe::ACT_SILU;
+}
+
 bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 struct Caps {
@@ -72,13 +81,13 @@ int check_weights(const moe_weights* w, int H, int activation, bool need_ptrs) {
     return fail(MOE_ERR_INVALID_ARG, "num_experts %d outside [1, 1024]", w->num_experts);
   if (w->quant != MOE_QUANT_NONE && w->quant != MOE_QUANT_FP8_G128)
     return fail(MOE_ERR_UNSUPPORTED, "weight quant %d not supported", w->quant);
-  if (activation != MOE_ACT_SILU_MUL && activation != MOE_ACT_SILU_NO_MUL)
+  if (activation < MOE_ACT_SILU_MUL || activation > MOE_ACT_GELU_NO_MUL)
     return fail(MOE_ERR_UNSUPPORTED, "activation %d not supported", activation);
   if (H <= 0 || H % 128) return fail(MOE_ERR_UNSUPPORTED, "H=%d must be a positive multiple of 128", H);
   if (H > 16384 || w->inter > 16384 || w->shared_inter > 16384)
     return fail(MOE_ERR_UNSUPPORTED, "H and I are limited to 16384 (fp8 scale staging, K > 16384)");
   const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
-  const bool gated = activation == MOE_ACT_SILU_MUL;
+  const bool gated = act_gated(activation);
   const int step = (!fp8 && gated) ? 64 : 128;
   if (w->inter <= 0 || w->inter % step)
     return fail(MOE_ERR_UNSUPPORTED, "I=%d must be a positive multiple of %d", w->inter, step);
@@ -129,7 +138,7 @@ struct SplitPlan {
 SplitPlan split_plan(int T, int H, int top_k, const moe_weights* w, int activation, int bm) {
   using namespace moe;
   const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
-  const bool gated = activation == MOE_ACT_SILU_MUL;
+  const bool gated = act_gated(activation);
   const int ktile = fp8 ? 128 : 64;
   const int E = w->num_experts, I = w->inter;
   const int64_t n = static_cast<int64_t>(T) * top_k;
@@ -216,7 +225,7 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
                 const StageEvents& se, hipStream_t s) {
   using namespace moe;
   const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
-  const bool gated = activation == MOE_ACT_SILU_MUL;
+  const bool gated = act_gated(activation);
   const size_t eb = fp8 ? 1 : 2;
   const int E = w->num_experts, I = w->inter;
   const int R = gated ? 2 * I : I;
@@ -232,7 +241,9 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
     if (fp8) launch_gemm_fp8(kind, gated, blk_m, bnz, p, max_mblk, s);
     else launch_gemm_bf16(kind, gated, blk_m, bnz, p, max_mblk, s);
   };
+  const int act = act_fn(activation);
   auto split = [&](GemmParams& g, int S, int64_t part_rows, int ldp) {
+    g.act = act;
     g.ksplit = S;
     g.partial = S > 1 ? part : nullptr;
     g.part_rows = part_rows;
@@ -262,7 +273,8 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   split(p, sp.s1, rows, R);
   launch(GEMM_Z_ROUTED, bm, bn1, p, cp.block_cap);
   if (sp.s1 > 1)
-    launch_splitk_z(part, sp.s1, rows, R, rows, ntp, sorted, nflat, T, I, gated, fp8, z, zs, I, s);
+    launch_splitk_z(part, sp.s1, rows, R, rows, ntp, sorted, nflat, T, I, gated, act, fp8, z, zs,
+                    I, s);
   se.mark(4);
   // routed second GEMM: z rows -> fused_expert_output[sorted row]
   const int bm2 = second_gemm_bm(fp8, bm);
@@ -312,8 +324,8 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
     split(d, sp.s3, T, Rs);
     launch(GEMM_Z_DENSE, dbm, bn3, d, mblk);
     if (sp.s3 > 1)
-      launch_splitk_z(part, sp.s3, T, Rs, T, nullptr, nullptr, 0, T, Is, gated, fp8, zsh, zshs, Is,
-                      s);
+      launch_splitk_z(part, sp.s3, T, Rs, T, nullptr, nullptr, 0, T, Is, gated, act, fp8, zsh, zshs,
+                      Is, s);
     GemmParams e{};
     e.a = static_cast<const uint8_t*>(zsh);
     e.a_scale = zshs;

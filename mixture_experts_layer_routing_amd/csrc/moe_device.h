@@ -113,4 +113,14 @@ __device__ __forceinline__ float silu_fast(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Exact GELU, v * Phi(v) = v/2 * (1 + erf(v / sqrt 2)), with the device erf.
+__device__ __forceinline__ float gelu_erf(float v) {
+  return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+}
+
+// The first GEMM's activation of the gate value (ACT_SILU or ACT_GELU).
+__device__ __forceinline__ float act_apply(int act, float v) {
+  return act == 1 ? gelu_erf(v) : silu_fast(v);
+}
+
 }  // namespace moe

@@ -5,9 +5,10 @@
 // GEMM cuts K into ksplit ranges and every workgroup writes an fp32 partial
 // tile.  These kernels sum the partials in split order (so the result does
 // not depend on scheduling) and apply the epilogue the GEMM would have
-// applied: SiLU-mul and the bf16 / fp8 G(128) store of z for the first GEMM,
+// applied: the activation (SiLU or GELU, times up when gated) and the bf16 /
+// fp8 G(128) store of z for the first GEMM,
 // the bf16 store of y to its fused_expert_output (or shared_out) row for
-// the second.  The arithmetic matches the GEMM epilogue (silu_fast,
+// the second.  The arithmetic matches the GEMM epilogue (act_apply,
 // hardware bf16 rounding, the same fp8 quantiser).
 //
 // One workgroup covers 2048 columns of one row, 8 per thread, so each
@@ -38,7 +39,8 @@ __device__ __forceinline__ void sum8(const float* p, int ksplit, int64_t slice, 
 __global__ __launch_bounds__(256) void splitk_z_kernel(
     const float* __restrict__ partial, int ksplit, int64_t slice, int ldp,
     const int32_t* __restrict__ ntp, const int32_t* __restrict__ sorted, int nflat, int T,
-    int inter, int gated, int fp8, void* __restrict__ z, float* __restrict__ z_scale, int ldz) {
+    int inter, int gated, int act, int fp8, void* __restrict__ z, float* __restrict__ z_scale,
+    int ldz) {
   const int r = blockIdx.x;
   const int rows = sorted ? ntp[0] : T;
   if (r >= rows) return;   // whole workgroup
@@ -56,10 +58,10 @@ __global__ __launch_bounds__(256) void splitk_z_kernel(
       float u[8];
       sum8(row + inter + c, ksplit, slice, u);
 #pragma unroll
-      for (int v = 0; v < 8; ++v) zv[v] = silu_fast(g[v]) * u[v];
+      for (int v = 0; v < 8; ++v) zv[v] = act_apply(act, g[v]) * u[v];
     } else {
 #pragma unroll
-      for (int v = 0; v < 8; ++v) zv[v] = silu_fast(g[v]);
+      for (int v = 0; v < 8; ++v) zv[v] = act_apply(act, g[v]);
     }
   }
   if (!fp8) {
@@ -115,12 +117,12 @@ __global__ __launch_bounds__(256) void splitk_y_kernel(
 
 void launch_splitk_z(const float* partial, int ksplit, int64_t part_rows, int ldp,
                      int64_t max_rows, const int32_t* ntp, const int32_t* sorted, int nflat,
-                     int T, int inter, bool gated, bool fp8, void* z, float* z_scale, int ldz,
-                     hipStream_t s) {
+                     int T, int inter, bool gated, int act, bool fp8, void* z, float* z_scale,
+                     int ldz, hipStream_t s) {
   if (max_rows <= 0) return;
   const dim3 grid(static_cast<unsigned>(max_rows), (inter + kCols - 1) / kCols);
   splitk_z_kernel<<<grid, 256, 0, s>>>(partial, ksplit, part_rows * ldp, ldp, ntp, sorted, nflat,
-                                       T, inter, gated ? 1 : 0, fp8 ? 1 : 0, z, z_scale, ldz);
+                                       T, inter, gated ? 1 : 0, act, fp8 ? 1 : 0, z, z_scale, ldz);
 }
 
 void launch_splitk_y(const float* partial, int ksplit, int64_t part_rows, int ldp,
