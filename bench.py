@@ -289,7 +289,7 @@ def main():
         stage[moe.STAGES[j]] = sum(vals) / len(vals)
     routed, shared = layer_flops(spec)
     tflops = (routed + shared) / (ms * 1e-3) / 1e12
-    dtype = "fp8" if spec.quant == "fp8" else "bf16"
+    dtype = "fp8" if spec.quant.startswith("fp8") else "bf16"
     g1_ms = stage["gemm1"]
     g1_tflops = gemm1_flops(spec) / (g1_ms * 1e-3) / 1e12
     traffic = None

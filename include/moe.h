@@ -61,11 +61,15 @@ typedef enum moe_scoring {
   MOE_SCORING_SIGMOID = 1   /* elementwise sigmoid */
 } moe_scoring;
 
+/* Activation quant formats of the quant-format key ("Fused MoE Kernel
+ * Features", table key): G(128) grouped by 128, A per activation token,
+ * T per tensor.  Every fp8 format takes E4M3 weights with one fp32 scale
+ * per 128x128 block of each matrix. */
 typedef enum moe_quant {
-  MOE_QUANT_NONE = 0,       /* bf16 activations and weights */
-  MOE_QUANT_FP8_G128 = 1    /* fp8 E4M3: activations with one fp32 scale per (row, 128-column
-                               group), the pages' "G(128)"; weights with one fp32 scale per
-                               128x128 block of each matrix */
+  MOE_QUANT_NONE = 0,        /* bf16 activations and weights */
+  MOE_QUANT_FP8_G128 = 1,    /* fp8 E4M3, one fp32 scale per (row, 128-column group): [T, H/128] */
+  MOE_QUANT_FP8_TOKEN = 2,   /* fp8 E4M3, one fp32 scale per row ("A"): [T] */
+  MOE_QUANT_FP8_TENSOR = 3   /* fp8 E4M3, one fp32 scale for the tensor ("T"): [1] */
 } moe_quant;
 
 /* The activation names of the fused-experts kernel table ("Fused MoE Kernel
@@ -87,7 +91,7 @@ typedef enum moe_activation {
  *   R = 2*inter for the gated activations MOE_ACT_SILU_MUL / MOE_ACT_GELU_MUL
  *       (rows [0, I) = gate W1, rows [I, 2I) = up W3),
  *       inter   for MOE_ACT_SILU_NO_MUL / MOE_ACT_GELU_NO_MUL (W1 only).
- *   w13        [E, R, H]   bf16 bits, or E4M3 codes (quant == MOE_QUANT_FP8_G128)
+ *   w13        [E, R, H]   bf16 bits, or E4M3 codes (any fp8 quant)
  *   w13_scale  [E, R/128, H/128] fp32 block scales (fp8 only, else NULL)
  *   w2         [E, H, I]
  *   w2_scale   [E, H/128, I/128]
@@ -138,6 +142,8 @@ int moe_route(const float* logits, int T, int E, int top_k, int scoring, int ren
  *   MOE_QUANT_NONE:     a1q [T, H] bf16 = a        (a1q_scale unused, may be NULL)
  *   MOE_QUANT_FP8_G128: per (t, g): s = max(amax, 1e-10) / 448 (fp32),
  *                       q = E4M3_rne_sat(a / s);   a1q [T, H] E4M3, a1q_scale [T, H/128] fp32
+ *   MOE_QUANT_FP8_TOKEN: the same rule with amax over the whole row; a1q_scale [T]
+ *   MOE_QUANT_FP8_TENSOR: the same rule with amax over all of a; a1q_scale [1]
  *   a1             [T, H] bf16
  *   topk_weights   [T, top_k] fp32 (read only when apply_router_weight_on_input)
  * Limits: H % 8 == 0; H % 128 == 0 for fp8.  a1q may alias a1 only for
@@ -185,11 +191,11 @@ size_t moe_align_workspace_bytes(int T, int top_k, int E, int block_m);
  *   h = W13[e] a[t] (fp32 accumulation), z = act(h),
  *   fused_expert_output[t, j, :] = bf16(W2[e] z)                  [T, top_k, H] bf16 out
  * z is held in bf16 (MOE_QUANT_NONE) or re-quantised to E4M3 G(128) along I
- * (fp8) between the two grouped GEMMs.  With a shared expert, additionally
+ * (every fp8 format) between the two grouped GEMMs.  With a shared expert, additionally
  *   shared_out[t, :] = bf16(W2s act(W13s s[t]))                    [T, H] bf16 out
  * where s = shared_in/shared_in_scale, the unweighted input in a1q's format
  * (pass a1q when the router weight was not applied on the input).
- *   a1q, a1q_scale      prepare's output ([T, H] + [T, H/128] fp32 for fp8)
+ *   a1q, a1q_scale      prepare's output ([T, H] + the format's scales for fp8)
  *   sorted_token_ids, block_expert_ids, num_tokens_post_padded: moe_align's
  *                       output for the same topk_ids and block_m
  *   workspace           moe_experts_workspace_bytes bytes

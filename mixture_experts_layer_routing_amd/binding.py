@@ -22,7 +22,16 @@ MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 
 SCORING = {"softmax": 0, "sigmoid": 1}
-QUANT = {"none": 0, "fp8": 1}
+QUANT = {"none": 0, "fp8": 1, "fp8_token": 2, "fp8_tensor": 3}
+
+
+def _is_fp8(quant):
+    return quant in ("fp8", "fp8_token", "fp8_tensor")
+
+
+def _act_scale_shape(quant, T, H):
+    """fp32 scales of an fp8 [T, H] activation: G(128), per token, per tensor."""
+    return {"fp8": (T, H // 128), "fp8_token": (T,), "fp8_tensor": (1,)}[quant]
 ACTIVATION = {"silu": 0, "silu_no_mul": 1, "gelu": 2, "gelu_no_mul": 3}
 NUM_STAGE_EVENTS = 8
 STAGES = ("start", "route", "prepare", "align", "gemm1", "gemm2", "shared", "finalize")
@@ -117,12 +126,14 @@ def _quant_of(t):
 
 
 def make_weights(w13, w2, w13_scale=None, w2_scale=None, shared_w13=None, shared_w2=None,
-                 shared_w13_scale=None, shared_w2_scale=None):
-    """Host struct of device pointers; the tensors must stay alive while it is used."""
+                 shared_w13_scale=None, shared_w2_scale=None, quant=None):
+    """Host struct of device pointers; the tensors must stay alive while it is used.
+    ``quant`` names the activation format for fp8 weights ("fp8" = G(128),
+    "fp8_token", "fp8_tensor"); by default it follows the weight dtype."""
     w = MoeWeights()
     w.num_experts = w13.shape[0]
     w.inter = w2.shape[2]
-    w.quant = _quant_of(w13)
+    w.quant = _quant_of(w13) if quant is None else QUANT[quant]
     w.shared_inter = 0 if shared_w2 is None else shared_w2.shape[1]
     w.w13, w.w13_scale, w.w2, w.w2_scale = _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale)
     w.shared_w13, w.shared_w13_scale = _ptr(shared_w13), _ptr(shared_w13_scale)
@@ -161,13 +172,14 @@ def moe_prepare(a1, topk_weights, apply_router_weight_on_input=False, quant="non
     dev = a1.device
     top_k = 1 if topk_weights is None else topk_weights.shape[1]
     if a1q is None:
-        a1q = torch.empty((T, H), dtype=torch.uint8 if quant == "fp8" else torch.bfloat16, device=dev)
-    if quant == "fp8" and a1q_scale is None:
-        a1q_scale = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+        a1q = torch.empty((T, H), dtype=torch.uint8 if _is_fp8(quant) else torch.bfloat16,
+                          device=dev)
+    if _is_fp8(quant) and a1q_scale is None:
+        a1q_scale = torch.empty(_act_scale_shape(quant, T, H), dtype=torch.float32, device=dev)
     _check(_lib.moe_prepare(_ptr(a1), T, H, _ptr(topk_weights), top_k,
                             int(apply_router_weight_on_input), QUANT[quant], _ptr(a1q),
                             _ptr(a1q_scale), _stream(stream)), "moe_prepare")
-    return a1q, (a1q_scale if quant == "fp8" else None)
+    return a1q, (a1q_scale if _is_fp8(quant) else None)
 
 
 def moe_align(topk_ids, E, block_m, stream=None):

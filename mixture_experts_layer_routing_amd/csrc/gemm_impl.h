@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   auto kloop_fp8 = [&](auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     static_assert(!FP8 || NSTAGE == 2, "fp8 runs two LDS stages");
-    if (tid < BM) sA[tid] = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kbase];
+    if (tid < BM) sA[tid] = p.a_scale[static_cast<int64_t>(a_srow) * p.sa_row + kbase * p.sa_k];
     if (nk > 0) dma(0, 0);
     int buf = 0;
     for (int kt = 0; kt < nk; ++kt) {
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       lds_barrier();
       float rsa = 0.f;
       if (kt + 1 < nk) {
-        if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * kblocks + kbase + kt + 1];
+        if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * p.sa_row + (kbase + kt + 1) * p.sa_k];
         dma(kt + 1, buf ^ 1);
       }
       // this k-tile's scales: weight blocks (gate, up) and the rows' activation

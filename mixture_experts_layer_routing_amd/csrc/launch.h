@@ -27,7 +27,9 @@ void launch_finalize(void* out, float* out_scale, int out_quant, const uint16_t*
 // One grouped-GEMM launch (see gemm_impl.h).
 struct GemmParams {
   const uint8_t* a;        // activation rows: bf16 or fp8 bytes, row length K
-  const float* a_scale;    // fp8: [rows][K/128]
+  const float* a_scale;    // fp8: scale of (row, k-block kb) at a_scale[row*sa_row + kb*sa_k]
+  int64_t sa_row;          //   G(128): (K/128, 1); per token: (1, 0); per tensor: (0, 0)
+  int sa_k;
   const uint8_t* w;        // expert 0's (or the shared expert's) weight matrix [n_w][K]
   const float* w_scale;    // fp8: [n_w/128][K/128] per expert
   int64_t w_stride;        // bytes between consecutive experts' matrices

@@ -47,6 +47,23 @@ struct Carve {
   }
 };
 
+bool quant_fp8(int quant) {
+  return quant == MOE_QUANT_FP8_G128 || quant == MOE_QUANT_FP8_TOKEN ||
+         quant == MOE_QUANT_FP8_TENSOR;
+}
+// fp32 scales of an fp8 [rows, K] activation in the given format
+size_t act_scale_count(int quant, int64_t rows, int K) {
+  if (quant == MOE_QUANT_FP8_G128) return static_cast<size_t>(rows) * (K / 128);
+  if (quant == MOE_QUANT_FP8_TOKEN) return static_cast<size_t>(rows);
+  if (quant == MOE_QUANT_FP8_TENSOR) return 1;
+  return 0;
+}
+// GEMM strides of those scales: (row, 128-deep k-block)
+void act_scale_strides(int quant, int K, int64_t* sa_row, int* sa_k) {
+  *sa_row = quant == MOE_QUANT_FP8_G128 ? K / 128 : (quant == MOE_QUANT_FP8_TOKEN ? 1 : 0);
+  *sa_k = quant == MOE_QUANT_FP8_G128 ? 1 : 0;
+}
+
 // Gated activations read the gate and up halves of W13; GELU or SiLU.
 bool act_gated(int activation) {
   return activation == MOE_ACT_SILU_MUL || activation == MOE_ACT_GELU_MUL;
@@ -79,14 +96,14 @@ int check_weights(const moe_weights* w, int H, int activation, bool need_ptrs) {
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
   if (w->num_experts < 1 || w->num_experts > 1024)
     return fail(MOE_ERR_INVALID_ARG, "num_experts %d outside [1, 1024]", w->num_experts);
-  if (w->quant != MOE_QUANT_NONE && w->quant != MOE_QUANT_FP8_G128)
+  if (w->quant != MOE_QUANT_NONE && !quant_fp8(w->quant))
     return fail(MOE_ERR_UNSUPPORTED, "weight quant %d not supported", w->quant);
   if (activation < MOE_ACT_SILU_MUL || activation > MOE_ACT_GELU_NO_MUL)
     return fail(MOE_ERR_UNSUPPORTED, "activation %d not supported", activation);
   if (H <= 0 || H % 128) return fail(MOE_ERR_UNSUPPORTED, "H=%d must be a positive multiple of 128", H);
   if (H > 16384 || w->inter > 16384 || w->shared_inter > 16384)
     return fail(MOE_ERR_UNSUPPORTED, "H and I are limited to 16384 (fp8 scale staging, K > 16384)");
-  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const bool fp8 = quant_fp8(w->quant);
   const bool gated = act_gated(activation);
   const int step = (!fp8 && gated) ? 64 : 128;
   if (w->inter <= 0 || w->inter % step)
@@ -137,7 +154,7 @@ struct SplitPlan {
 
 SplitPlan split_plan(int T, int H, int top_k, const moe_weights* w, int activation, int bm) {
   using namespace moe;
-  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const bool fp8 = quant_fp8(w->quant);
   const bool gated = act_gated(activation);
   const int ktile = fp8 ? 128 : 64;
   const int E = w->num_experts, I = w->inter;
@@ -180,7 +197,7 @@ SplitPlan split_plan(int T, int H, int top_k, const moe_weights* w, int activati
 size_t experts_ws(int T, int H, int top_k, const moe_weights* w, int activation, int bm,
                   Carve& c, void** z, float** zs, void** zsh, float** zshs, float** part,
                   size_t* offs = nullptr) {
-  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const bool fp8 = quant_fp8(w->quant);
   const size_t eb = fp8 ? 1 : 2;
   const Caps cp = capacities(T, top_k, w->num_experts, bm);
   const int64_t rows = cp.block_cap * bm;
@@ -224,7 +241,7 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
                 const int32_t* ntp, int bm, uint16_t* feo, uint16_t* shared_out, void* ws,
                 const StageEvents& se, hipStream_t s) {
   using namespace moe;
-  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const bool fp8 = quant_fp8(w->quant);
   const bool gated = act_gated(activation);
   const size_t eb = fp8 ? 1 : 2;
   const int E = w->num_experts, I = w->inter;
@@ -253,6 +270,7 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   GemmParams p{};
   p.a = static_cast<const uint8_t*>(a1q);
   p.a_scale = a1q_scale;
+  act_scale_strides(w->quant, H, &p.sa_row, &p.sa_k);
   p.w = static_cast<const uint8_t*>(w->w13);
   p.w_scale = w->w13_scale;
   p.w_stride = static_cast<int64_t>(R) * H * eb;
@@ -281,6 +299,7 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   GemmParams q{};
   q.a = static_cast<const uint8_t*>(z);
   q.a_scale = zs;
+  act_scale_strides(MOE_QUANT_FP8_G128, I, &q.sa_row, &q.sa_k);   // z: G(128) along I
   q.w = static_cast<const uint8_t*>(w->w2);
   q.w_scale = w->w2_scale;
   q.w_stride = static_cast<int64_t>(H) * I * eb;
@@ -309,6 +328,7 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
     GemmParams d{};
     d.a = static_cast<const uint8_t*>(shared_in);
     d.a_scale = shared_in_scale;
+    act_scale_strides(w->quant, H, &d.sa_row, &d.sa_k);
     d.w = static_cast<const uint8_t*>(w->shared_w13);
     d.w_scale = w->shared_w13_scale;
     d.K = H;
@@ -329,6 +349,7 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
     GemmParams e{};
     e.a = static_cast<const uint8_t*>(zsh);
     e.a_scale = zshs;
+    act_scale_strides(MOE_QUANT_FP8_G128, Is, &e.sa_row, &e.sa_k);
     e.w = static_cast<const uint8_t*>(w->shared_w2);
     e.w_scale = w->shared_w2_scale;
     e.K = Is;
@@ -374,7 +395,7 @@ int moe_pick_block_m(int T, int top_k, int num_experts, int quant) {
   const int64_t avg = (static_cast<int64_t>(T) * top_k + num_experts - 1) / num_experts;
   if (avg <= 16) return 16;
   if (avg <= 32) return 32;
-  if (quant == MOE_QUANT_FP8_G128) return avg <= 96 ? 64 : 128;
+  if (quant_fp8(quant)) return avg <= 96 ? 64 : 128;
   return avg <= 64 ? 64 : 256;
 }
 
@@ -399,17 +420,19 @@ int moe_prepare(const uint16_t* a1, int T, int H, const float* topk_weights, int
                 hipStream_t stream) {
   g_err[0] = 0;
   if (T < 0 || H <= 0 || H % 8) return fail(MOE_ERR_INVALID_ARG, "T=%d H=%d", T, H);
-  if (quant != MOE_QUANT_NONE && quant != MOE_QUANT_FP8_G128)
+  if (quant != MOE_QUANT_NONE && !quant_fp8(quant))
     return fail(MOE_ERR_UNSUPPORTED, "quant %d not supported", quant);
-  if (quant == MOE_QUANT_FP8_G128 && H % 128)
-    return fail(MOE_ERR_INVALID_ARG, "fp8 G(128) needs H %% 128 == 0 (H=%d)", H);
+  if (quant_fp8(quant) && H % 128)
+    return fail(MOE_ERR_INVALID_ARG, "fp8 needs H %% 128 == 0 (H=%d)", H);
+  if (quant == MOE_QUANT_FP8_TOKEN && H > 16384)
+    return fail(MOE_ERR_UNSUPPORTED, "per-token fp8 holds a row in registers: H=%d > 16384", H);
   if (apply_router_weight_on_input && top_k != 1)
     return fail(MOE_ERR_INVALID_ARG, "router weight on the input needs top_k == 1 (got %d)", top_k);
   if (T == 0) return MOE_OK;
   if (!a1 || !a1q || (apply_router_weight_on_input && !topk_weights) ||
-      (quant == MOE_QUANT_FP8_G128 && !a1q_scale))
+      (quant_fp8(quant) && !a1q_scale))
     return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
-  if (quant == MOE_QUANT_FP8_G128 && static_cast<const void*>(a1) == a1q)
+  if (quant_fp8(quant) && static_cast<const void*>(a1) == a1q)
     return fail(MOE_ERR_INVALID_ARG, "a1q may not alias a1 for fp8");
   moe::launch_prepare(a1, T, H, topk_weights, apply_router_weight_on_input ? 1 : 0, quant, a1q,
                       a1q_scale, stream);
@@ -489,7 +512,7 @@ int moe_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   if (!valid_block_m(block_m)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", block_m);
   if (int st = check_weights(weights, H, activation, true)) return st;
   if (top_k > weights->num_experts) return fail(MOE_ERR_INVALID_ARG, "top_k > E");
-  const bool fp8 = weights->quant == MOE_QUANT_FP8_G128;
+  const bool fp8 = quant_fp8(weights->quant);
   if (fp8 && block_m > 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts support block_m <= 128");
   if (static_cast<int64_t>(T) * top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
   if (T == 0) return MOE_OK;
@@ -552,7 +575,7 @@ struct ForwardLayout {
 size_t forward_layout(int T, int H, int top_k, const moe_weights* w, int activation, int bm,
                       int woi, void* base, ForwardLayout* L) {
   Carve c(base);
-  const bool fp8 = w->quant == MOE_QUANT_FP8_G128;
+  const bool fp8 = quant_fp8(w->quant);
   const size_t eb = fp8 ? 1 : 2;
   const int E = w->num_experts;
   const int64_t n = static_cast<int64_t>(T) * top_k;
@@ -560,12 +583,12 @@ size_t forward_layout(int T, int H, int top_k, const moe_weights* w, int activat
   L->ids = static_cast<int32_t*>(c.take(n * 4));
   L->tw = static_cast<float*>(c.take(n * 4));
   L->a1q = c.take(static_cast<size_t>(T) * H * eb);
-  L->a1q_scale = fp8 ? static_cast<float*>(c.take(static_cast<size_t>(T) * (H / 128) * 4)) : nullptr;
+  L->a1q_scale = fp8 ? static_cast<float*>(c.take(act_scale_count(w->quant, T, H) * 4)) : nullptr;
   L->shin = nullptr;
   L->shin_scale = nullptr;
   if (w->shared_inter > 0 && woi && fp8) {
     L->shin = c.take(static_cast<size_t>(T) * H);
-    L->shin_scale = static_cast<float*>(c.take(static_cast<size_t>(T) * (H / 128) * 4));
+    L->shin_scale = static_cast<float*>(c.take(act_scale_count(w->quant, T, H) * 4));
   }
   L->counts = static_cast<int32_t*>(c.take(E * 4));
   L->offsets = static_cast<int32_t*>(c.take((E + 1) * 4));
@@ -619,7 +642,7 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
   if (static_cast<int64_t>(T) * top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
   const int bm = block_m ? block_m : moe_pick_block_m(T, top_k, E, weights->quant);
   if (!valid_block_m(bm)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", bm);
-  const bool fp8 = weights->quant == MOE_QUANT_FP8_G128;
+  const bool fp8 = quant_fp8(weights->quant);
   if (fp8 && bm > 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts support block_m <= 128");
   if (T == 0) return MOE_OK;
   if (!x || !logits || !output || (out_quant == MOE_QUANT_FP8_G128 && !output_scale))
@@ -640,7 +663,7 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
   moe::launch_route(logits, T, E, top_k, scoring, renormalize ? 1 : 0, L.ids, L.tw, stream);
   se.mark(1);
   const void* a1q = x;
-  if (quant == MOE_QUANT_FP8_G128 || apply_router_weight_on_input) {
+  if (quant_fp8(quant) || apply_router_weight_on_input) {
     moe::launch_prepare(x, T, H, L.tw, apply_router_weight_on_input ? 1 : 0, quant, L.a1q,
                         L.a1q_scale, stream);
     a1q = L.a1q;

@@ -45,11 +45,15 @@ from .moe import (  # noqa: F401
     route,
     prepare,
     quantize_g128,
+    quantize_token,
+    quantize_tensor,
     dequant_g128,
+    dequant_scaled,
     align,
     align_capacity,
     experts,
     finalize,
     forward,
     silu,
+    gelu,
 )

@@ -114,6 +114,50 @@ def dequant_g128(codes, scales):
     return v * np.repeat(np.asarray(scales, np.float64), GROUP, axis=1)
 
 
+def _quantize_scale(v32, amax):
+    """E4M3 codes of float32 values v32 under float32 amax (broadcastable),
+    with the scale rule of quantize_g128."""
+    s = (np.maximum(amax, QUANT_EPS) / np.float32(E4M3_MAX)).astype(np.float32)
+    q = e4m3_encode_sat((v32 / s).astype(np.float32).astype(np.float64))
+    return q, s
+
+
+def quantize_token(values):
+    """fp8 E4M3 with one float32 scale per row over all its columns: the
+    "A" (per activation token) format of the quant-format key.  Same scale
+    and code rule as quantize_g128.  Returns (codes [R, C], scales [R, 1])."""
+    v32 = np.asarray(values, dtype=np.float64).astype(np.float32)
+    amax = np.abs(v32).max(axis=1, keepdims=True) if v32.size else np.zeros((v32.shape[0], 1),
+                                                                             np.float32)
+    return _quantize_scale(v32, amax)
+
+
+def quantize_tensor(values):
+    """fp8 E4M3 with one float32 scale for the whole tensor: the "T" (per
+    tensor) format of the quant-format key.  Returns (codes, scales [1, 1])."""
+    v32 = np.asarray(values, dtype=np.float64).astype(np.float32)
+    amax = np.abs(v32).max(keepdims=True).reshape(1, 1) if v32.size else np.zeros((1, 1),
+                                                                                  np.float32)
+    return _quantize_scale(v32, amax)
+
+
+def dequant_scaled(codes, scales):
+    """E4M3 codes [R, C] with scales in any of the three formats: G(128)
+    [R, C/128], per token [R, 1] or per tensor [1, 1] -> float64."""
+    scales = np.asarray(scales, np.float64)
+    v = e4m3_decode(codes)
+    C = v.shape[1]
+    if scales.shape[1] == 1:
+        return v * scales                     # broadcast over columns (and rows)
+    if scales.shape[1] * GROUP != C:
+        raise ValueError("scales do not match the G(128) layout")
+    return v * np.repeat(scales, GROUP, axis=1)
+
+
+# activation formats of prepare's fp8 quantiser
+QUANTISERS = {"fp8": quantize_g128, "fp8_token": quantize_token, "fp8_tensor": quantize_tensor}
+
+
 def prepare(x_bits, topk_weights, apply_router_weight_on_input, quant="none"):
     """No-DP/EP prepare ("[vLLM] MoE Oracle & Prepare/Finalize", the
     MoEPrepareAndFinalizeNoDPEPModular.prepare code): when the router weight
@@ -123,7 +167,8 @@ def prepare(x_bits, topk_weights, apply_router_weight_on_input, quant="none"):
 
     The bf16 x bf16 product is exact in float64, so the result has a single
     rounding.  quant="none" returns bf16 bits and no scales; quant="fp8"
-    returns (codes, G(128) scales)."""
+    returns (codes, G(128) scales), "fp8_token" (codes, per-token scales
+    [rows, 1]) and "fp8_tensor" (codes, one scale [1, 1])."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     a_bits = x_bits
     if apply_router_weight_on_input:
@@ -134,8 +179,8 @@ def prepare(x_bits, topk_weights, apply_router_weight_on_input, quant="none"):
         a_bits = f64_to_bf16_bits(bf16_bits_to_f64(x_bits) * wq)
     if quant == "none":
         return a_bits, None
-    if quant == "fp8":
-        return quantize_g128(bf16_bits_to_f64(a_bits))
+    if quant in QUANTISERS:
+        return QUANTISERS[quant](bf16_bits_to_f64(a_bits))
     raise ValueError(quant)
 
 
@@ -217,11 +262,20 @@ def dequant_weight(w, scale):
     return v * np.repeat(np.repeat(s, WBLOCK, axis=0), WBLOCK, axis=1)[:v.shape[0], :v.shape[1]]
 
 
+def _scale_rows(scale, tok):
+    """The scales of rows ``tok``: a single-row scale array (per tensor)
+    serves every row."""
+    if scale is None:
+        return None
+    scale = np.asarray(scale)
+    return scale if scale.shape[0] == 1 else scale[tok]
+
+
 def dequant_act(a, a_scale):
-    """prepare's output -> float64 rows."""
+    """prepare's output -> float64 rows (any of the three fp8 scale formats)."""
     if a_scale is None:
         return bf16_bits_to_f64(a)
-    return dequant_g128(a, a_scale)
+    return dequant_scaled(a, a_scale)
 
 
 def _round_intermediate(z, mode, quant):
@@ -287,7 +341,7 @@ def experts(a1q, a1q_scale, topk_ids, w13, w13_scale, w2, w2_scale,
     H = a1q.shape[1]
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     out = np.zeros((T, k, H), dtype=np.uint16)
-    a_tok = dequant_act(a1q[tok], None if a1q_scale is None else a1q_scale[tok])
+    a_tok = dequant_act(a1q[tok], _scale_rows(a1q_scale, tok))
     sub_ids = ids[tok]                                   # [n, k]
     for e in np.unique(sub_ids):
         rr, jj = np.nonzero(sub_ids == e)                # rows of the subset
@@ -299,7 +353,7 @@ def experts(a1q, a1q_scale, topk_ids, w13, w13_scale, w2, w2_scale,
     if shared is not None:
         sa = shared["a"][tok]
         ss = shared.get("a_scale")
-        a_sh = dequant_act(sa, None if ss is None else ss[tok])
+        a_sh = dequant_act(sa, _scale_rows(ss, tok))
         w13s = dequant_weight(shared["w13"], shared.get("w13_scale"))
         w2s = dequant_weight(shared["w2"], shared.get("w2_scale"))
         y = expert_mlp(a_sh, w13s, w2s, activation, mode, quant)
@@ -376,24 +430,28 @@ def forward(x_bits, logits, w, top_k, scoring, renormalize, block_m,
     al = align(ids, E, block_m)
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     tok = np.arange(x_bits.shape[0]) if tokens is None else np.asarray(tokens)
-    a_sub, s_sub = prepare(x_bits[tok], tw[tok], apply_router_weight_on_input, quant)
     T, H = x_bits.shape
-    a1q = np.zeros((T, H), dtype=a_sub.dtype)
-    a1q[tok] = a_sub
-    a1q_scale = None
-    if s_sub is not None:
-        a1q_scale = np.zeros((T, H // GROUP), dtype=np.float32)
-        a1q_scale[tok] = s_sub
+
+    def prep(weights):
+        # the per-tensor scale depends on every token: quantise them all
+        if quant == "fp8_tensor":
+            return prepare(x_bits, weights, apply_router_weight_on_input and weights is not None,
+                           quant)
+        a_sub, s_sub = prepare(x_bits[tok], None if weights is None else weights[tok],
+                               apply_router_weight_on_input and weights is not None, quant)
+        a = np.zeros((T, H), dtype=a_sub.dtype)
+        a[tok] = a_sub
+        if s_sub is None:
+            return a, None
+        sc = np.zeros((T, s_sub.shape[1]), dtype=np.float32)
+        sc[tok] = s_sub
+        return a, sc
+
+    a1q, a1q_scale = prep(tw)
     shared = None
     if w.get("shared_w13") is not None:
         if apply_router_weight_on_input:
-            sa_sub, ss_sub = prepare(x_bits[tok], None, False, quant)
-            sa = np.zeros_like(a1q)
-            sa[tok] = sa_sub
-            ss = None
-            if ss_sub is not None:
-                ss = np.zeros_like(a1q_scale)
-                ss[tok] = ss_sub
+            sa, ss = prep(None)
         else:
             sa, ss = a1q, a1q_scale
         shared = dict(a=sa, a_scale=ss, w13=w["shared_w13"], w13_scale=w.get("shared_w13_scale"),

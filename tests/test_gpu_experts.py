@@ -29,9 +29,10 @@ def _announce(name):
     print(f"[case] {name}", file=sys.stderr, flush=True)
 
 
-def _weights(moe, d):
+def _weights(moe, d, quant=None):
     return moe.make_weights(*(d.get(k) for k in ("w13", "w2", "w13_scale", "w2_scale", "shared_w13",
-                                                 "shared_w2", "shared_w13_scale", "shared_w2_scale")))
+                                                 "shared_w2", "shared_w13_scale", "shared_w2_scale")),
+                            quant=None if quant in (None, "none") else quant)
 
 
 def _host_w(d):
@@ -51,7 +52,7 @@ def _ref_f64(spec, r):
 
 
 def _path(spec):
-    return "fp8" if (spec.quant == "fp8" or spec.out_quant == "fp8") else "bf16"
+    return "fp8" if (spec.quant.startswith("fp8") or spec.out_quant == "fp8") else "bf16"
 
 
 # ------------------------------------------------------ experts stage, reduced
@@ -80,7 +81,7 @@ def test_experts_stage_reduced(spec, BM):
         shared = dict(a=sa, a_scale=ss, w13=hw["shared_w13"], w13_scale=hw.get("shared_w13_scale"),
                       w2=hw["shared_w2"], w2_scale=hw.get("shared_w2_scale"))
     al = moe.moe_align(ids, spec.E, BM)
-    w = _weights(moe, dd)
+    w = _weights(moe, dd, spec.quant)
     ws = torch.empty(moe.binding.lib().moe_experts_workspace_bytes(
         spec.T, spec.H, spec.top_k, moe.binding.ctypes.byref(w),
         moe.binding.ACTIVATION[spec.activation], BM), dtype=torch.uint8, device=DEV)
@@ -92,7 +93,7 @@ def test_experts_stage_reduced(spec, BM):
     for mode in ("exact", "mirrored"):
         refs[mode] = oracle.experts(ra, rs, rid, hw["w13"], hw.get("w13_scale"), hw["w2"],
                                     hw.get("w2_scale"), spec.activation, mode, shared)
-    fp8 = spec.quant == "fp8"
+    fp8 = spec.quant.startswith("fp8")
     path = "fp8" if fp8 else "bf16"
     check_tolerance(f64_of_bf16(feo), f64_of_bf16(refs["exact"][0]), f64_of_bf16(refs["mirrored"][0]),
                     path, f"{spec.name} fused_expert_output", elementwise=not fp8)
@@ -156,7 +157,7 @@ def test_forward_reduced(spec):
     moe = _moe()
     d = make_layer_inputs(spec)
     dd = {k: v.to(DEV) for k, v in d.items()}
-    w = _weights(moe, dd)
+    w = _weights(moe, dd, spec.quant)
     hw = _host_w(d)
     refs = {mode: oracle.forward(to_numpy_bits(d["x"]), d["logits"].numpy(), hw, spec.top_k,
                                  spec.scoring, spec.renormalize, 16,
@@ -173,7 +174,7 @@ def test_forward_reduced(spec):
         torch.cuda.synchronize()
         check_tolerance(_out_f64(spec, out, scale), _ref_f64(spec, refs["exact"]),
                         _ref_f64(spec, refs["mirrored"]), _path(spec), f"{spec.name} BM={bm}",
-                        elementwise=spec.quant != "fp8",
+                        elementwise=not spec.quant.startswith("fp8"),
                         min_identical=0.9 if _path(spec) == "bf16" else None,
                         allowance=finalize_flip_allowance(refs["mirrored"],
                                                           to_numpy_bits(d.get("gamma"))))
@@ -183,7 +184,7 @@ def test_forward_zero_tokens_is_a_no_op():
     moe = _moe()
     spec = PARITY_CASES[1]
     d = {k: v.to(DEV) for k, v in make_layer_inputs(spec).items()}
-    w = _weights(moe, d)
+    w = _weights(moe, d, spec.quant)
     x = torch.empty((0, spec.H), dtype=torch.bfloat16, device=DEV)
     lg = torch.empty((0, spec.E), dtype=torch.float32, device=DEV)
     out, _, _ = moe.moe_forward(x, lg, w, spec.top_k)
@@ -197,7 +198,7 @@ def test_forward_token_permutation_equivariance():
     moe = _moe()
     spec = PARITY_CASES[1]
     d = {k: v.to(DEV) for k, v in make_layer_inputs(spec).items()}
-    w = _weights(moe, d)
+    w = _weights(moe, d, spec.quant)
     perm = torch.randperm(spec.T, generator=torch.Generator().manual_seed(0)).to(DEV)
     a, _, _ = moe.moe_forward(d["x"], d["logits"], w, spec.top_k, spec.scoring, spec.renormalize,
                               block_m=16)
@@ -213,7 +214,7 @@ def test_forward_unit_weight_on_input_matches_no_flag():
     moe = _moe()
     spec = PARITY_CASES[3]
     d = {k: v.to(DEV) for k, v in make_layer_inputs(spec).items()}
-    w = _weights(moe, d)
+    w = _weights(moe, d, spec.quant)
     a, _, _ = moe.moe_forward(d["x"], d["logits"], w, 1, "softmax", True, True)
     b, _, _ = moe.moe_forward(d["x"], d["logits"], w, 1, "softmax", True, False)
     torch.cuda.synchronize()
@@ -240,7 +241,7 @@ def test_forward_degenerate_and_limit_shapes(spec):
     moe = _moe()
     d = make_layer_inputs(spec)
     dd = {k: v.to(DEV) for k, v in d.items()}
-    w = _weights(moe, dd)
+    w = _weights(moe, dd, spec.quant)
     hw = _host_w(d)
     refs = {mode: oracle.forward(to_numpy_bits(d["x"]), d["logits"].numpy(), hw, spec.top_k,
                                  spec.scoring, spec.renormalize, 16,
@@ -253,7 +254,7 @@ def test_forward_degenerate_and_limit_shapes(spec):
     torch.cuda.synchronize()
     check_tolerance(_out_f64(spec, out, scale), _ref_f64(spec, refs["exact"]),
                     _ref_f64(spec, refs["mirrored"]), _path(spec), spec.name,
-                    elementwise=spec.quant != "fp8",
+                    elementwise=not spec.quant.startswith("fp8"),
                     allowance=finalize_flip_allowance(refs["mirrored"]))
 
 
@@ -289,7 +290,7 @@ def test_forward_full_size_sampled(spec):
     _announce(f"full {spec.name}")
     moe = _moe()
     d, hw = _full_inputs(spec)
-    w = _weights(moe, d)
+    w = _weights(moe, d, spec.quant)
     bm = moe.moe_pick_block_m(spec.T, spec.top_k, spec.E, spec.quant)
     out, scale, _ = moe.moe_forward(d["x"], d["logits"], w, spec.top_k, spec.scoring,
                                     spec.renormalize, spec.apply_router_weight_on_input,
@@ -316,7 +317,7 @@ def test_forward_full_size_sampled(spec):
             for mode in ("exact", "mirrored")}
     got = _out_f64(spec, out, scale, sample)
     rep = check_tolerance(got, _ref_f64(spec, refs["exact"]), _ref_f64(spec, refs["mirrored"]),
-                          _path(spec), spec.name, elementwise=spec.quant != "fp8",
+                          _path(spec), spec.name, elementwise=not spec.quant.startswith("fp8"),
                           min_identical=0.9 if _path(spec) == "bf16" else None,
                           allowance=finalize_flip_allowance(refs["mirrored"],
                                                             to_numpy_bits(d.get("gamma"))))

@@ -79,7 +79,10 @@ def test_route_rejects_bad_arguments():
 @pytest.mark.parametrize("T,H,flag,quant", [
     (16, 128, False, "fp8"), (203, 768, False, "fp8"), (64, 7168, False, "fp8"),
     (157, 640, True, "none"), (128, 5120, True, "none"), (77, 512, True, "fp8"),
-    (1, 7168, False, "fp8"), (3, 8, True, "none")])
+    (1, 7168, False, "fp8"), (3, 8, True, "none"),
+    (203, 768, False, "fp8_token"), (64, 7168, True, "fp8_token"), (5, 16384, False, "fp8_token"),
+    (1, 128, False, "fp8_token"), (203, 768, False, "fp8_tensor"), (77, 5120, True, "fp8_tensor"),
+    (4096, 7168, False, "fp8_tensor"), (1, 128, False, "fp8_tensor")])
 def test_prepare_bit_exact(T, H, flag, quant):
     _announce(f"prepare T={T} H={H} flag={flag} {quant}")
     moe = _moe()
@@ -91,8 +94,8 @@ def test_prepare_bit_exact(T, H, flag, quant):
     torch.cuda.synchronize()
     rq, rs = oracle.prepare(to_numpy_bits(x), None if tw is None else tw.numpy(), flag, quant)
     np.testing.assert_array_equal(to_numpy_bits(q), rq)
-    if quant == "fp8":
-        np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    if quant.startswith("fp8"):
+        np.testing.assert_array_equal(s.cpu().numpy().reshape(rs.shape), rs)
 
 
 def test_prepare_zero_group_and_constant_group():

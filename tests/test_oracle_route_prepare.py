@@ -149,3 +149,45 @@ def test_fp8_round_trip_error_bound():
     assert np.all(err[~normal] <= srep[~normal] * (2.0 ** -10 + 2.0 ** -30))
     amax_code = np.abs(codecs.e4m3_decode(q)).reshape(64, 8, 128).max(axis=2)
     assert np.all(amax_code == 448.0)       # every group's largest element hits the top code
+
+
+def test_per_token_and_per_tensor_quantisers_match_torch_float32_and_cast():
+    """The "A" and "T" formats: one scale per token row / for the whole
+    tensor, same rule as G(128), checked against torch float32 ops + the
+    float8_e4m3fn cast."""
+    rng = np.random.default_rng(5)
+    x = _bf16(rng.normal(size=(24, 384)) * rng.uniform(0.01, 100, size=(24, 1)))
+    xf = x.float()
+    q, s = oracle.prepare(_bits(x), None, False, "fp8_token")
+    s_ref = torch.clamp(xf.abs().amax(dim=1, keepdim=True), min=1e-10) / 448.0
+    assert s.shape == (24, 1)
+    np.testing.assert_array_equal(s, s_ref.numpy())
+    np.testing.assert_array_equal(q, (xf / s_ref).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    q, s = oracle.prepare(_bits(x), None, False, "fp8_tensor")
+    s_ref = torch.clamp(xf.abs().amax(), min=1e-10).reshape(1, 1) / 448.0
+    assert s.shape == (1, 1)
+    np.testing.assert_array_equal(s, s_ref.numpy())
+    np.testing.assert_array_equal(q, (xf / s_ref).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_scale_formats_nest():
+    """A row's per-token scale is the largest of its G(128) scales, and the
+    per-tensor scale the largest per-token scale (amax and the scale rule are
+    monotone)."""
+    rng = np.random.default_rng(6)
+    v = rng.normal(size=(17, 640)) * rng.uniform(1e-3, 1e3, size=(17, 5)).repeat(128, axis=1)
+    _, sg = oracle.quantize_g128(v)
+    _, st = oracle.quantize_token(v)
+    _, sT = oracle.quantize_tensor(v)
+    np.testing.assert_array_equal(st[:, 0], sg.max(axis=1))
+    assert sT[0, 0] == st.max()
+
+
+def test_dequant_scaled_broadcasts_each_format():
+    rng = np.random.default_rng(7)
+    v = rng.normal(size=(6, 256))
+    for quant in (oracle.quantize_g128, oracle.quantize_token, oracle.quantize_tensor):
+        q, s = quant(v)
+        deq = oracle.moe.dequant_scaled(q, s)
+        full = np.broadcast_to(np.repeat(s, 128, axis=1) if s.shape[1] == 2 else s, v.shape)
+        np.testing.assert_array_equal(deq, codecs.e4m3_decode(q) * full)

@@ -22,7 +22,8 @@ class WorkloadSpec:
     top_k: int
     scoring: str = "softmax"    # "softmax" | "sigmoid"
     renormalize: bool = True
-    quant: str = "none"         # "none" | "fp8" (G(128) acts, 128x128 weight blocks)
+    quant: str = "none"         # "none" | "fp8" (G(128) acts) | "fp8_token" | "fp8_tensor"
+                                # (fp8: 128x128 weight blocks)
     activation: str = "silu"    # "silu" (SiLU-mul) | "silu_no_mul" | "gelu" | "gelu_no_mul"
     apply_router_weight_on_input: bool = False
     shared_I: int = 0           # 0 = no shared expert
@@ -111,4 +112,9 @@ PARITY_CASES = [
     WorkloadSpec("gelu_no_mul_fp8_mini", 10, T=93, H=512, I=256, E=16, top_k=1,
                  renormalize=False, apply_router_weight_on_input=True, quant="fp8",
                  activation="gelu_no_mul"),
+    # the per-token ("A") and per-tensor ("T") activation formats
+    WorkloadSpec("fp8_token_mini", 16, T=117, H=768, I=256, E=32, top_k=8, scoring="sigmoid",
+                 quant="fp8_token", shared_I=256, hot_experts=4, hot_fraction=0.05),
+    WorkloadSpec("fp8_tensor_mini", 17, T=89, H=512, I=384, E=16, top_k=1, renormalize=False,
+                 apply_router_weight_on_input=True, quant="fp8_tensor", shared_I=256),
 ]

@@ -80,7 +80,7 @@ def make_layer_inputs(spec: WorkloadSpec, device="cpu", weights=True):
         for name, idx, n, rows, cols, fan_in in mats:
             g = _gen(base + idx, device)
             std = 1.0 / np.sqrt(fan_in)
-            if spec.quant == "fp8":
+            if spec.quant.startswith("fp8"):
                 c, s = _fp8_matrix_stack(n, rows, cols, std, g, device)
                 out[name], out[name + "_scale"] = c, s
             else:
