@@ -227,6 +227,50 @@ int moe_experts_workspace_layout(int T, int H, int top_k, const moe_weights* wei
                                  int activation, int block_m, size_t* out);
 
 /*
+ * moe_experts_batched -- the experts stage on the batched activation format
+ * ("Fused MoE Modular Kernel" / "Fused MoE Kernel Features": prepare emits
+ * either the standard or the batched format, and the batched experts
+ * kernels take one batch of rows per expert).  With M = max_tokens, rows
+ * [0, expert_num_tokens[e]) of batch e are expert e's input; for each such
+ * row m
+ *   out[e, m, :] = bf16(W2[e] act(W13[e] a[e, m]))           (fp32 accumulation)
+ * exactly as moe_experts computes one routed row (z held in bf16, or E4M3
+ * G(128) along I for every fp8 format).  Rows m >= expert_num_tokens[e] of
+ * `out` are not written.
+ *   a                  [E, M, H] bf16, or E4M3 codes for an fp8 format
+ *   a_scale            fp8 only: G(128) [E, M, H/128]; per token [E, M];
+ *                      per tensor [1] (fp32); the format is weights->quant
+ *   expert_num_tokens  [E] int32 on the device; values are clamped to [0, M]
+ *   out                [E, M, H] bf16
+ *   block_m            GEMM row block, 0 = moe_pick_block_m(M, 1, 1, quant)
+ *   workspace          moe_experts_batched_workspace_bytes bytes
+ * The shared expert of `weights` (if any) is not run: it reads the
+ * token-major input, which this format does not carry.  M == 0 is a no-op.
+ * Limits: as moe_experts; E * (M + block_m) <= 2^30.
+ */
+int moe_experts_batched(const void* a, const float* a_scale, const int32_t* expert_num_tokens,
+                        int max_tokens, int H, const moe_weights* weights /* host */,
+                        int activation, int block_m, uint16_t* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+/* (host) workspace moe_experts_batched needs (0 for invalid arguments). */
+size_t moe_experts_batched_workspace_bytes(int max_tokens, int H, const moe_weights* weights,
+                                           int activation, int block_m);
+/*
+ * (host) Where moe_experts_batched keeps its row schedule and the
+ * intermediate z inside its workspace (readable after a call until the
+ * workspace is reused).  out[4] receives byte offsets from the workspace
+ * start (SIZE_MAX when absent):
+ *   out[0] the schedule, int32 [rows]: row r of z is batch row
+ *          sorted[r] = e*M + m, or the pad sentinel E*M (experts in index
+ *          order, each padded to a multiple of block_m)
+ *   out[1] z [rows, I] bf16 (E4M3 codes for fp8)
+ *   out[2] its G(128) scales [rows, I/128] fp32 (fp8 only)
+ *   out[3] rows = E * ceil(M / block_m) * block_m (a count, not an offset)
+ */
+int moe_experts_batched_workspace_layout(int max_tokens, int H, const moe_weights* weights,
+                                         int activation, int block_m, size_t* out);
+
+/*
  * moe_finalize -- the no-DP/EP finalize (weight-and-reduce over the top-k
  * expert rows) with the flashinfer finalize fusions:
  *   acc[t] = sum_j w'[t,j] * y[t,j,:]   (slot order; w' = 1 when the weight was

@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     moe_align,
     moe_align_capacity,
     moe_experts,
+    moe_experts_batched,
+    moe_experts_batched_workspace_layout,
     moe_experts_workspace_layout,
     moe_finalize,
     moe_forward,

@@ -76,6 +76,12 @@ def _load():
                                                c_int, c_int]),
         "moe_experts_workspace_layout": (c_int, [c_int, c_int, c_int, ctypes.POINTER(MoeWeights),
                                                  c_int, c_int, ctypes.POINTER(c_sz)]),
+        "moe_experts_batched": (c_int, [c_vp, c_vp, c_vp, c_int, c_int, ctypes.POINTER(MoeWeights),
+                                        c_int, c_int, c_vp, c_vp, c_sz, c_vp]),
+        "moe_experts_batched_workspace_bytes": (c_sz, [c_int, c_int, ctypes.POINTER(MoeWeights),
+                                                       c_int, c_int]),
+        "moe_experts_batched_workspace_layout": (c_int, [c_int, c_int, ctypes.POINTER(MoeWeights),
+                                                         c_int, c_int, ctypes.POINTER(c_sz)]),
         "moe_finalize": (c_int, [c_vp, c_vp, c_int, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                  c_vp, c_vp, c_vp, c_vp, c_f32, c_vp]),
         "moe_forward": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
@@ -241,6 +247,41 @@ def moe_experts_workspace_layout(T, H, top_k, weights, activation="silu", block_
     none = (1 << (8 * ctypes.sizeof(c_sz))) - 1
     v = [None if x == none else x for x in out]
     return dict(z=v[0], z_scale=v[1], shared_z=v[2], shared_z_scale=v[3], rows=v[4])
+
+
+def moe_experts_batched(a, a_scale, expert_num_tokens, weights, activation="silu", block_m=0,
+                        out=None, workspace=None, stream=None):
+    """Experts on the batched format: ``a`` [E, M, H] (bf16, or E4M3 codes
+    as uint8 with ``a_scale`` in weights' format), ``expert_num_tokens`` [E]
+    int32.  Returns ``out`` [E, M, H] bf16; rows past an expert's count are
+    left as they were (uninitialised when ``out`` is not given).  With
+    ``workspace`` given (a uint8 tensor) the schedule and z stay readable in
+    it afterwards (see moe_experts_batched_workspace_layout)."""
+    E, M, H = a.shape
+    dev = a.device
+    if out is None:
+        out = torch.empty((E, M, H), dtype=torch.bfloat16, device=dev)
+    act = ACTIVATION[activation]
+    wsb = _lib.moe_experts_batched_workspace_bytes(M, H, ctypes.byref(weights), act, block_m)
+    ws = workspace
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(_lib.moe_experts_batched(_ptr(a), _ptr(a_scale), _ptr(expert_num_tokens), M, H,
+                                    ctypes.byref(weights), act, block_m, _ptr(out), _ptr(ws), wsb,
+                                    _stream(stream)), "moe_experts_batched")
+    return out
+
+
+def moe_experts_batched_workspace_layout(M, H, weights, activation="silu", block_m=0):
+    """Byte offsets inside moe_experts_batched's workspace: dict(sorted, z,
+    z_scale, rows); None = absent."""
+    out = (c_sz * 4)()
+    _check(_lib.moe_experts_batched_workspace_layout(M, H, ctypes.byref(weights),
+                                                     ACTIVATION[activation], block_m, out),
+           "moe_experts_batched_workspace_layout")
+    none = (1 << (8 * ctypes.sizeof(c_sz))) - 1
+    v = [None if x == none else x for x in out]
+    return dict(sorted=v[0], z=v[1], z_scale=v[2], rows=v[3])
 
 
 def moe_finalize(fused_expert_output, topk_weights, topk_ids=None,

@@ -19,6 +19,11 @@ void launch_align(const int32_t* ids, int64_t n, int E, int BM, int32_t* counts,
                   int32_t* offsets, int32_t* sorted, int64_t sorted_cap, int32_t* block_ids,
                   int64_t block_cap, int32_t* ntp, void* ws, hipStream_t s);
 
+// Block schedule of the batched format (counts [E] -> sorted rows e*M + m,
+// block owners, padded row total), block_cap = E * ceil(M / bm).
+void launch_batched_schedule(const int32_t* counts, int E, int M, int bm, int64_t block_cap,
+                             int32_t* sorted, int32_t* block_expert, int32_t* ntp, hipStream_t s);
+
 void launch_finalize(void* out, float* out_scale, int out_quant, const uint16_t* y,
                      const float* w, int T, int k, int H, int woi, const uint16_t* sh,
                      const uint16_t* res, uint16_t* res_out, const uint16_t* gamma, float eps,

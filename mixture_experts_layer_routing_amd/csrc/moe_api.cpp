@@ -85,6 +85,22 @@ Caps capacities(int T, int top_k, int E, int bm) {
   return {cap, (cap + bm - 1) / bm};
 }
 
+// The rows the routed GEMMs walk.  Standard format: align's schedule over
+// the T*top_k flat rows of a [T, H] activation (top_k rows per token).
+// Batched format: the schedule built from per-expert counts over the E*M
+// rows of an [E, M, H] activation, each its own "token" (top_k 1).
+struct Routed {
+  int T, top_k;
+  Caps cp;
+};
+
+Routed standard_rows(int T, int top_k, int E, int bm) { return {T, top_k, capacities(T, top_k, E, bm)}; }
+
+Routed batched_rows(int E, int M, int bm) {
+  const int64_t nb = (static_cast<int64_t>(M) + bm - 1) / bm;
+  return {E * M, 1, {E * nb * bm, E * nb}};
+}
+
 int dense_block_m(int T) {
   if (T <= 16) return 16;
   if (T <= 32) return 32;
@@ -152,18 +168,19 @@ struct SplitPlan {
   size_t partial_bytes;
 };
 
-SplitPlan split_plan(int T, int H, int top_k, const moe_weights* w, int activation, int bm) {
+SplitPlan split_plan(const Routed& rt, int T, int H, const moe_weights* w, int activation,
+                     int bm) {
   using namespace moe;
   const bool fp8 = quant_fp8(w->quant);
   const bool gated = act_gated(activation);
   const int ktile = fp8 ? 128 : 64;
   const int E = w->num_experts, I = w->inter;
-  const int64_t n = static_cast<int64_t>(T) * top_k;
+  const int64_t n = static_cast<int64_t>(rt.T) * rt.top_k;
   const double eb = fp8 ? 1.0 : 2.0;
   const int64_t touched = std::min<int64_t>(E, n);
   auto est_blocks = [&](int b) { return touched + (n - touched) / b; };
   SplitPlan sp{1, 1, 1, 1, 0};
-  const int64_t rows = capacities(T, top_k, E, bm).block_cap * bm;
+  const int64_t rows = rt.cp.block_cap * bm;
   const int64_t R = gated ? 2 * I : I;
   const int bn1 = gemm_tile_n(GEMM_Z_ROUTED, fp8, gated, bm, I);
   sp.s1 = pick_ksplit(est_blocks(bm) * (I / bn1), H, ktile, rows, R,
@@ -194,13 +211,12 @@ SplitPlan split_plan(int T, int H, int top_k, const moe_weights* w, int activati
 // Workspace of the experts stage: z for the routed rows and for the shared
 // expert, in the GEMM input format of the second GEMM, then the split-K
 // partial sums (shared by the launches, which run in stream order).
-size_t experts_ws(int T, int H, int top_k, const moe_weights* w, int activation, int bm,
+size_t experts_ws(const Routed& rt, int T, int H, const moe_weights* w, int activation, int bm,
                   Carve& c, void** z, float** zs, void** zsh, float** zshs, float** part,
                   size_t* offs = nullptr) {
   const bool fp8 = quant_fp8(w->quant);
   const size_t eb = fp8 ? 1 : 2;
-  const Caps cp = capacities(T, top_k, w->num_experts, bm);
-  const int64_t rows = cp.block_cap * bm;
+  const int64_t rows = rt.cp.block_cap * bm;
   const size_t start = c.used;
   const size_t none = static_cast<size_t>(-1);
   size_t o[5] = {none, none, none, none, static_cast<size_t>(rows)};
@@ -221,7 +237,7 @@ size_t experts_ws(int T, int H, int top_k, const moe_weights* w, int activation,
       o[3] = c.last - start;
     }
   }
-  const SplitPlan sp = split_plan(T, H, top_k, w, activation, bm);
+  const SplitPlan sp = split_plan(rt, T, H, w, activation, bm);
   *part = sp.partial_bytes ? static_cast<float*>(c.take(sp.partial_bytes)) : nullptr;
   if (offs) for (int i = 0; i < 5; ++i) offs[i] = o[i];
   return c.used - start;
@@ -236,7 +252,7 @@ struct StageEvents {
 };
 
 int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
-                const float* shared_in_scale, int T, int H, int top_k, const moe_weights* w,
+                const float* shared_in_scale, const Routed& rt, int T, int H, const moe_weights* w,
                 int activation, const int32_t* sorted, const int32_t* block_expert,
                 const int32_t* ntp, int bm, uint16_t* feo, uint16_t* shared_out, void* ws,
                 const StageEvents& se, hipStream_t s) {
@@ -244,16 +260,16 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   const bool fp8 = quant_fp8(w->quant);
   const bool gated = act_gated(activation);
   const size_t eb = fp8 ? 1 : 2;
-  const int E = w->num_experts, I = w->inter;
+  const int I = w->inter;
   const int R = gated ? 2 * I : I;
   Carve c(ws);
   void *z, *zsh;
   float *zs, *zshs, *part;
-  experts_ws(T, H, top_k, w, activation, bm, c, &z, &zs, &zsh, &zshs, &part);
-  const SplitPlan sp = split_plan(T, H, top_k, w, activation, bm);
-  const Caps cp = capacities(T, top_k, E, bm);
+  experts_ws(rt, T, H, w, activation, bm, c, &z, &zs, &zsh, &zshs, &part);
+  const SplitPlan sp = split_plan(rt, T, H, w, activation, bm);
+  const Caps& cp = rt.cp;
   const int64_t rows = cp.block_cap * bm;
-  const int nflat = T * top_k;
+  const int nflat = rt.T * rt.top_k;
   auto launch = [&](int kind, int blk_m, int bnz, const GemmParams& p, int64_t max_mblk) {
     if (fp8) launch_gemm_fp8(kind, gated, blk_m, bnz, p, max_mblk, s);
     else launch_gemm_bf16(kind, gated, blk_m, bnz, p, max_mblk, s);
@@ -282,8 +298,8 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   p.sorted = sorted;
   p.block_expert = block_expert;
   p.ntp = ntp;
-  p.T = T;
-  p.top_k = top_k;
+  p.T = rt.T;
+  p.top_k = rt.top_k;
   p.align_bm = bm;
   p.out = z;
   p.out_scale = zs;
@@ -291,8 +307,8 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   split(p, sp.s1, rows, R);
   launch(GEMM_Z_ROUTED, bm, bn1, p, cp.block_cap);
   if (sp.s1 > 1)
-    launch_splitk_z(part, sp.s1, rows, R, rows, ntp, sorted, nflat, T, I, gated, act, fp8, z, zs,
-                    I, s);
+    launch_splitk_z(part, sp.s1, rows, R, rows, ntp, sorted, nflat, rt.T, I, gated, act, fp8, z,
+                    zs, I, s);
   se.mark(4);
   // routed second GEMM: z rows -> fused_expert_output[sorted row]
   const int bm2 = second_gemm_bm(fp8, bm);
@@ -311,14 +327,15 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   q.sorted = sorted;
   q.block_expert = block_expert;
   q.ntp = ntp;
-  q.T = T;
-  q.top_k = top_k;
+  q.T = rt.T;
+  q.top_k = rt.top_k;
   q.align_bm = bm;
   q.out = feo;
   q.ldo = H;
   split(q, sp.s2, rows, H);
   launch(GEMM_Y_ROUTED, bm2, bn2, q, cp.block_cap * (bm / bm2));
-  if (sp.s2 > 1) launch_splitk_y(part, sp.s2, rows, H, rows, ntp, sorted, nflat, T, H, feo, H, s);
+  if (sp.s2 > 1)
+    launch_splitk_y(part, sp.s2, rows, H, rows, ntp, sorted, nflat, rt.T, H, feo, H, s);
   se.mark(5);
   if (w->shared_inter > 0) {
     const int Is = w->shared_inter;
@@ -485,7 +502,8 @@ size_t moe_experts_workspace_bytes(int T, int H, int top_k, const moe_weights* w
   Carve c(nullptr);
   void *z, *zsh;
   float *zs, *zshs, *part;
-  return experts_ws(T, H, top_k, weights, activation, block_m, c, &z, &zs, &zsh, &zshs, &part);
+  return experts_ws(standard_rows(T, top_k, weights->num_experts, block_m), T, H, weights,
+                    activation, block_m, c, &z, &zs, &zsh, &zshs, &part);
 }
 
 int moe_experts_workspace_layout(int T, int H, int top_k, const moe_weights* weights,
@@ -497,7 +515,8 @@ int moe_experts_workspace_layout(int T, int H, int top_k, const moe_weights* wei
   Carve c(nullptr);
   void *z, *zsh;
   float *zs, *zshs, *part;
-  experts_ws(T, H, top_k, weights, activation, block_m, c, &z, &zs, &zsh, &zshs, &part, out);
+  experts_ws(standard_rows(T, top_k, weights->num_experts, block_m), T, H, weights, activation,
+             block_m, c, &z, &zs, &zsh, &zshs, &part, out);
   return MOE_OK;
 }
 
@@ -524,10 +543,114 @@ int moe_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   const size_t need = moe_experts_workspace_bytes(T, H, top_k, weights, activation, block_m);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "experts workspace %zu < %zu", workspace_bytes, need);
-  return run_experts(a1q, a1q_scale, shared_in, shared_in_scale, T, H, top_k, weights, activation,
-                     sorted_token_ids, block_expert_ids, num_tokens_post_padded, block_m,
+  return run_experts(a1q, a1q_scale, shared_in, shared_in_scale,
+                     standard_rows(T, top_k, weights->num_experts, block_m), T, H, weights,
+                     activation, sorted_token_ids, block_expert_ids, num_tokens_post_padded, block_m,
                      fused_expert_output, shared_out, workspace, StageEvents{nullptr, stream},
                      stream);
+}
+
+namespace {
+
+// Workspace of the batched experts: the block schedule, then the experts
+// stage's own pieces.  The shared expert is not part of this stage.
+struct BatchedLayout {
+  int32_t *sorted, *blocks, *ntp;
+  void* experts_ws;
+  size_t experts_ws_bytes;
+  size_t offs[5];   // experts_ws pieces, from the workspace start (SIZE_MAX = absent)
+};
+
+moe_weights routed_only(const moe_weights* w) {
+  moe_weights r = *w;
+  r.shared_inter = 0;
+  r.shared_w13 = r.shared_w2 = nullptr;
+  r.shared_w13_scale = r.shared_w2_scale = nullptr;
+  return r;
+}
+
+int batched_block_m(int M, int block_m, int quant) {
+  return block_m ? block_m : moe_pick_block_m(M, 1, 1, quant);
+}
+
+size_t batched_layout(int M, int H, const moe_weights* w, int activation, int bm, void* base,
+                      BatchedLayout* L) {
+  const Routed rt = batched_rows(w->num_experts, M, bm);
+  Carve c(base);
+  L->sorted = static_cast<int32_t*>(c.take(static_cast<size_t>(rt.cp.sorted_cap) * 4));
+  L->blocks = static_cast<int32_t*>(c.take(static_cast<size_t>(rt.cp.block_cap) * 4));
+  L->ntp = static_cast<int32_t*>(c.take(4));
+  Carve sub(nullptr);
+  void *z, *zsh;
+  float *zs, *zshs, *part;
+  L->experts_ws_bytes =
+      experts_ws(rt, 0, H, w, activation, bm, sub, &z, &zs, &zsh, &zshs, &part, L->offs);
+  L->experts_ws = c.take(L->experts_ws_bytes);
+  for (int i = 0; i < 4; ++i)
+    if (L->offs[i] != static_cast<size_t>(-1)) L->offs[i] += c.last;
+  return c.used;
+}
+
+}  // namespace
+
+size_t moe_experts_batched_workspace_bytes(int max_tokens, int H, const moe_weights* weights,
+                                           int activation, int block_m) {
+  if (!weights || max_tokens < 0) return 0;
+  if (check_weights(weights, H, activation, false) != MOE_OK) return 0;
+  const moe_weights w = routed_only(weights);
+  const int bm = batched_block_m(max_tokens, block_m, w.quant);
+  if (!valid_block_m(bm)) return 0;
+  if (static_cast<int64_t>(w.num_experts) * (max_tokens + bm) > (1 << 30)) return 0;
+  BatchedLayout L;
+  return batched_layout(max_tokens, H, &w, activation, bm, nullptr, &L);
+}
+
+int moe_experts_batched_workspace_layout(int max_tokens, int H, const moe_weights* weights,
+                                         int activation, int block_m, size_t* out) {
+  g_err[0] = 0;
+  if (!out || max_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "bad arguments");
+  if (int st = check_weights(weights, H, activation, false)) return st;
+  const moe_weights w = routed_only(weights);
+  const int bm = batched_block_m(max_tokens, block_m, w.quant);
+  if (!valid_block_m(bm)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", bm);
+  BatchedLayout L;
+  batched_layout(max_tokens, H, &w, activation, bm, nullptr, &L);
+  out[0] = 0;   // the schedule is the first piece
+  out[1] = L.offs[0];
+  out[2] = L.offs[1];
+  out[3] = L.offs[4];
+  return MOE_OK;
+}
+
+int moe_experts_batched(const void* a, const float* a_scale, const int32_t* expert_num_tokens,
+                        int max_tokens, int H, const moe_weights* weights, int activation,
+                        int block_m, uint16_t* out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  g_err[0] = 0;
+  if (max_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "max_tokens=%d < 0", max_tokens);
+  if (int st = check_weights(weights, H, activation, true)) return st;
+  const moe_weights w = routed_only(weights);
+  const int bm = batched_block_m(max_tokens, block_m, w.quant);
+  if (!valid_block_m(bm)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", bm);
+  const bool fp8 = quant_fp8(w.quant);
+  if (fp8 && bm > 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts support block_m <= 128");
+  const int E = w.num_experts;
+  if (static_cast<int64_t>(E) * (max_tokens + bm) > (1 << 30))
+    return fail(MOE_ERR_INVALID_ARG, "E*(max_tokens+block_m) too large");
+  if (max_tokens == 0) return MOE_OK;
+  if (!a || !expert_num_tokens || !out || (fp8 && !a_scale))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  BatchedLayout L;
+  const size_t need = batched_layout(max_tokens, H, &w, activation, bm, nullptr, &L);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "batched experts workspace %zu < %zu", workspace_bytes, need);
+  batched_layout(max_tokens, H, &w, activation, bm, workspace, &L);
+  const Routed rt = batched_rows(E, max_tokens, bm);
+  moe::launch_batched_schedule(expert_num_tokens, E, max_tokens, bm, rt.cp.block_cap, L.sorted,
+                               L.blocks, L.ntp, stream);
+  if (int st = check_launch("moe_experts_batched schedule")) return st;
+  return run_experts(a, a_scale, nullptr, nullptr, rt, 0, H, &w, activation, L.sorted, L.blocks,
+                     L.ntp, bm, out, nullptr, L.experts_ws, StageEvents{nullptr, stream}, stream);
 }
 
 int moe_finalize(void* output, float* output_scale, int out_quant,
@@ -599,7 +722,8 @@ size_t forward_layout(int T, int H, int top_k, const moe_weights* w, int activat
   Carve sub(nullptr);
   void *z, *zsh;
   float *zs, *zshs, *part;
-  L->experts_ws_bytes = experts_ws(T, H, top_k, w, activation, bm, sub, &z, &zs, &zsh, &zshs, &part);
+  L->experts_ws_bytes = experts_ws(standard_rows(T, top_k, E, bm), T, H, w, activation, bm, sub, &z,
+                                   &zs, &zsh, &zshs, &part);
   L->experts_ws = c.take(L->experts_ws_bytes);
   L->feo = static_cast<uint16_t*>(c.take(static_cast<size_t>(n) * H * 2));
   L->shared_out = w->shared_inter > 0 ? static_cast<uint16_t*>(c.take(static_cast<size_t>(T) * H * 2))
@@ -685,8 +809,8 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
   moe::launch_align(L.ids, n, E, bm, L.counts, L.offsets, L.sorted, cp.sorted_cap, L.blocks,
                     cp.block_cap, L.ntp, L.align_ws, stream);
   se.mark(3);
-  int st = run_experts(a1q, L.a1q_scale, shin, shin_scale, T, H, top_k, weights, activation,
-                       L.sorted, L.blocks, L.ntp, bm, L.feo, L.shared_out, L.experts_ws, se, stream);
+  int st = run_experts(a1q, L.a1q_scale, shin, shin_scale, standard_rows(T, top_k, E, bm), T, H,
+                       weights, activation, L.sorted, L.blocks, L.ntp, bm, L.feo, L.shared_out, L.experts_ws, se, stream);
   if (st) return st;
   moe::launch_finalize(output, output_scale, out_quant, L.feo, L.tw, T, top_k, H,
                        apply_router_weight_on_input ? 1 : 0, L.shared_out, residual, residual_out,

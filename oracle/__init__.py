@@ -52,6 +52,7 @@ from .moe import (  # noqa: F401
     align,
     align_capacity,
     experts,
+    experts_batched,
     finalize,
     forward,
     silu,

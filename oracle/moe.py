@@ -362,6 +362,42 @@ def experts(a1q, a1q_scale, topk_ids, w13, w13_scale, w2, w2_scale,
     return out, shared_out
 
 
+def experts_batched(a, a_scale, expert_num_tokens, w13, w13_scale, w2, w2_scale,
+                    activation="silu", mode="exact", experts_subset=None):
+    """The experts stage on the batched activation format: prepare may hand
+    the experts one batch per expert instead of the token-major rows ("Fused
+    MoE Kernel Features": the standard and batched output formats of
+    prepare, and the batched experts kernels of the fused-experts table).
+    Batch e holds expert e's input rows in its first count[e] positions;
+    for each of them y = W2[e] act(W13[e] a[e, m]) in bf16, the same MLP the
+    standard-format stage runs per routed row.  Positions past the count
+    carry nothing and stay zero here.  Reading: a count outside [0, M] is
+    clamped into it (a batch has M rows).
+
+    a [E, M, H] bf16 bits or E4M3 codes; a_scale None (bf16) or the fp8
+    scales as [E, M, H/128] (G(128)), [E, M, 1] (per token) or [1, 1] (per
+    tensor).  ``experts_subset`` restricts the work to some experts (the
+    others' batches stay zero).  Returns out bits [E, M, H]."""
+    a = np.asarray(a)
+    E, M, H = a.shape
+    counts = np.clip(np.asarray(expert_num_tokens, dtype=np.int64), 0, M)
+    quant = "none" if a_scale is None else "fp8"
+    out = np.zeros((E, M, H), dtype=np.uint16)
+    for e in (range(E) if experts_subset is None else experts_subset):
+        c = int(counts[e])
+        if c == 0:
+            continue
+        s = None
+        if a_scale is not None:
+            s = np.asarray(a_scale)
+            s = s if s.ndim == 2 else s[e, :c]
+        rows = dequant_act(a[e, :c], s)
+        w13e = dequant_weight(w13[e], None if w13_scale is None else w13_scale[e])
+        w2e = dequant_weight(w2[e], None if w2_scale is None else w2_scale[e])
+        out[e, :c] = f64_to_bf16_bits(expert_mlp(rows, w13e, w2e, activation, mode, quant))
+    return out
+
+
 # --------------------------------------------------------------------------
 # finalize
 # --------------------------------------------------------------------------

@@ -98,6 +98,26 @@ def make_layer_inputs(spec: WorkloadSpec, device="cpu", weights=True):
     return out
 
 
+def make_batched_inputs(spec: WorkloadSpec, M, device="cpu"):
+    """Inputs of the experts stage on the batched format: ``a`` bf16
+    [E, M, H] ~N(0,1), every row drawn (rows past an expert's count too,
+    which the stage must ignore); ``expert_num_tokens`` int32 [E] ~U{0..M},
+    then expert 0 set empty and expert E-1 full when E > 1; plus the
+    weights of make_layer_inputs for ``spec``."""
+    base = 1000 * spec.config
+    out = make_layer_inputs(spec.with_T(0), device)
+    del out["x"], out["logits"]
+    g = _gen(base + 13, device)
+    out["a"] = _randn((spec.E, M, spec.H), g, device).to(torch.bfloat16)
+    g = _gen(base + 14, "cpu")
+    counts = torch.randint(0, M + 1, (spec.E,), generator=g, dtype=torch.int32)
+    if spec.E > 1:
+        counts[0] = 0
+        counts[-1] = M
+    out["expert_num_tokens"] = counts.to(device)
+    return out
+
+
 def make_finalize_inputs(spec: FinalizeSpec, device="cpu"):
     """Inputs of the finalize fusion: fused_expert_output bf16 [T,k,H] ~N(0,1);
     topk_weights f32 [T,k] = softmax of N(0,1) draws (drawn and normalised
