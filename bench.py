@@ -271,18 +271,46 @@ def main():
     out, _, ws = step()
     for _ in range(a.warmup):
         step(ws=ws, out=out)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.NUM_STAGE_EVENTS)]
-           for _ in range(a.steps)]
+    # the timed steps: plain moe_forward calls, nothing recorded between kernels
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(events=evs[i], ws=ws, out=out)
+        step(ws=ws, out=out)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / a.steps
+    # the same number of steps again with an event between stages: the
+    # per-stage times and the GEMM-1 duration of the roofline (the events
+    # themselves add small gaps, so the step time above is taken without them)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.NUM_STAGE_EVENTS)]
+           for _ in range(a.steps)]
+    for i in range(a.steps):
+        step(events=evs[i], ws=ws, out=out)
+    torch.cuda.synchronize()
+    # the same step replayed as one graph launch (moe_forward_graph_*): the
+    # kernels and buffers are identical, only the per-kernel host submission
+    # is gone -- the rate a decode loop sees
+    gstream = torch.cuda.Stream()
+    with torch.cuda.stream(gstream):
+        graph = moe.ForwardGraph(d["x"], d["logits"], w, spec.top_k, spec.scoring,
+                                 spec.renormalize, spec.apply_router_weight_on_input,
+                                 spec.activation, bm, d.get("residual"), d.get("gamma"), spec.eps,
+                                 spec.out_quant)
+        for _ in range(a.warmup):
+            graph.launch(gstream)
+    torch.cuda.synchronize()
+    gstart, gstop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gstart.record(gstream)
+    for _ in range(a.steps):
+        graph.launch(gstream)
+    gstop.record(gstream)
+    torch.cuda.synchronize()
+    graph_ms = gstart.elapsed_time(gstop) / a.steps
+    graph.close()
+    del graph
     stage = {}
     for j in range(1, moe.NUM_STAGE_EVENTS):
         vals = [evs[i][j - 1].elapsed_time(evs[i][j]) for i in range(a.steps)]
@@ -320,6 +348,8 @@ def main():
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_TFLOPS[dtype], 4),
         "stage_ms": {k: round(v, 4) for k, v in stage.items()},
+        "graph": {"ms_per_step": round(graph_ms, 4),
+                  "tokens_per_s": round(spec.T / (graph_ms * 1e-3), 1)},
         "wall_s": round(wall, 3),
         "roofline": {"kernel": "routed GEMM-1 (gate+up, SiLU-mul fused)", "bound": "mfma",
                      "achieved": round(g1_tflops, 2), "peak": PEAK_TFLOPS[dtype],

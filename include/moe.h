@@ -314,6 +314,36 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
 size_t moe_forward_workspace_bytes(int T, int H, int top_k, const moe_weights* weights,
                                    int activation, int block_m,
                                    int apply_router_weight_on_input);
+/*
+ * moe_forward_graph_* -- the whole layer as one launch ("[vLLM] MoE Oracle &
+ * Prepare/Finalize", modular vs monolithic: the monolithic mode runs the
+ * layer fused into a single launch).  create captures moe_forward, for
+ * exactly these sizes, weights and buffers, into an executable HIP graph;
+ * launch replays it on any stream with one call, with no per-kernel host
+ * work -- what a decode step needs, where the layer's kernels are shorter
+ * than their submission.  The graph reads and writes the very buffers given
+ * here, so the caller refreshes x and logits (and residual, gamma) in place
+ * before each launch and reads output afterwards; replays on one stream
+ * run in order, and two replays of one graph must not overlap.
+ *   Arguments as moe_forward (no stage events); stream must be a created
+ *   stream (capture is not allowed on the null stream), and nothing else may
+ *   be enqueued on it from this thread while create runs.
+ *   graph (host out): opaque handle; release it with moe_forward_graph_destroy.
+ * Errors: moe_forward's checks (nothing captured, *graph = NULL) or
+ * MOE_ERR_HIP from capture/instantiation.
+ */
+typedef struct moe_graph moe_graph;
+int moe_forward_graph_create(const uint16_t* x, const float* logits, int T, int H, int top_k,
+                             int scoring, int renormalize, int apply_router_weight_on_input,
+                             const moe_weights* weights /* host */, int activation, int block_m,
+                             const uint16_t* residual, const uint16_t* gamma, float eps,
+                             int out_quant, void* output, float* output_scale,
+                             uint16_t* residual_out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, moe_graph** graph /* host out */);
+int moe_forward_graph_launch(moe_graph* graph, hipStream_t stream);
+/* Releases the graph (NULL is a no-op); no replay of it may still be pending. */
+int moe_forward_graph_destroy(moe_graph* graph);
+
 /* (host) the block_m moe_forward uses when given 0, by the average rows per
  * expert a = T*top_k/E: 16 (a <= 16), 32 (a <= 32), then bf16: 64 (a <= 64)
  * else 256; fp8: 64 (a <= 96) else 128.  quant is a moe_quant. */

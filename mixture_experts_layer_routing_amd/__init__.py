@@ -6,6 +6,7 @@ raises ImportError when the library has not been built.
 """
 
 from .binding import (  # noqa: F401
+    ForwardGraph,
     MoeError,
     MoeWeights,
     make_weights,

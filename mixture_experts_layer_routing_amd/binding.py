@@ -89,6 +89,12 @@ def _load():
                                 c_vp, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp]),
         "moe_forward_workspace_bytes": (c_sz, [c_int, c_int, c_int, ctypes.POINTER(MoeWeights),
                                                c_int, c_int, c_int]),
+        "moe_forward_graph_create": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                             ctypes.POINTER(MoeWeights), c_int, c_int, c_vp, c_vp,
+                                             c_f32, c_int, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp,
+                                             ctypes.POINTER(c_vp)]),
+        "moe_forward_graph_launch": (c_int, [c_vp, c_vp]),
+        "moe_forward_graph_destroy": (c_int, [c_vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -342,3 +348,58 @@ def moe_forward(x, logits, weights, top_k, scoring="softmax", renormalize=True,
                             _ptr(residual_out), _ptr(workspace), wsb, ev, _stream(stream)),
            "moe_forward")
     return output, (output_scale if out_quant == "fp8" else None), workspace
+
+
+class ForwardGraph:
+    """moe_forward captured once into a HIP graph (moe_forward_graph_create)
+    and replayed with one launch.  The graph is bound to the tensors given
+    here: write new inputs into ``x`` / ``logits`` (and ``residual``,
+    ``gamma``) in place, call launch(), then read ``output``.  Capture runs on
+    ``stream`` (default: the current stream), which must not be the null
+    stream."""
+
+    def __init__(self, x, logits, weights, top_k, scoring="softmax", renormalize=True,
+                 apply_router_weight_on_input=False, activation="silu", block_m=0, residual=None,
+                 gamma=None, eps=1e-6, out_quant="none", want_residual_out=False, stream=None):
+        T, H = x.shape
+        dev = x.device
+        self.output = torch.empty((T, H), dtype=torch.uint8 if out_quant == "fp8" else torch.bfloat16,
+                                  device=dev)
+        self.output_scale = (torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+                             if out_quant == "fp8" else None)
+        self.residual_out = (torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+                             if want_residual_out else None)
+        wsb = moe_forward_workspace_bytes(T, H, top_k, weights, activation, block_m,
+                                          apply_router_weight_on_input)
+        self.workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        self._keep = (x, logits, weights, residual, gamma)
+        self._h = c_vp()
+        st = stream if stream is not None else torch.cuda.current_stream()
+        if st.cuda_stream == 0:
+            raise ValueError("graph capture needs a created stream, not the null stream")
+        _check(_lib.moe_forward_graph_create(
+            _ptr(x), _ptr(logits), T, H, top_k, SCORING[scoring], int(renormalize),
+            int(apply_router_weight_on_input), ctypes.byref(weights), ACTIVATION[activation],
+            block_m, _ptr(residual), _ptr(gamma), float(eps), QUANT[out_quant], _ptr(self.output),
+            _ptr(self.output_scale), _ptr(self.residual_out), _ptr(self.workspace), wsb,
+            _stream(st), ctypes.byref(self._h)), "moe_forward_graph_create")
+
+    def launch(self, stream=None):
+        """Enqueue one replay; returns (output, output_scale)."""
+        if not self._h:
+            raise RuntimeError("graph was closed")
+        _check(_lib.moe_forward_graph_launch(self._h, _stream(stream)), "moe_forward_graph_launch")
+        return self.output, self.output_scale
+
+    def close(self):
+        """Wait for pending replays, then release the graph."""
+        if self._h:
+            torch.cuda.synchronize(self.output.device)
+            h, self._h = self._h, c_vp()
+            _check(_lib.moe_forward_graph_destroy(h), "moe_forward_graph_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <new>
 
 #include "launch.h"
 
@@ -817,6 +818,71 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
                        gamma, eps, stream);
   se.mark(7);
   return check_launch("moe_forward");
+}
+
+struct moe_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+int moe_forward_graph_create(const uint16_t* x, const float* logits, int T, int H, int top_k,
+                             int scoring, int renormalize, int apply_router_weight_on_input,
+                             const moe_weights* weights, int activation, int block_m,
+                             const uint16_t* residual, const uint16_t* gamma, float eps,
+                             int out_quant, void* output, float* output_scale,
+                             uint16_t* residual_out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, moe_graph** graph) {
+  g_err[0] = 0;
+  if (!graph) return fail(MOE_ERR_INVALID_ARG, "graph is NULL");
+  *graph = nullptr;
+  if (!stream) return fail(MOE_ERR_INVALID_ARG, "capture needs a created stream, not the null stream");
+  hipError_t e = hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+  const int st = moe_forward(x, logits, T, H, top_k, scoring, renormalize,
+                             apply_router_weight_on_input, weights, activation, block_m, residual,
+                             gamma, eps, out_quant, output, output_scale, residual_out, workspace,
+                             workspace_bytes, nullptr, stream);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(stream, &g);
+  if (st != MOE_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return st;   // moe_forward's own message
+  }
+  if (e != hipSuccess || !g)
+    return fail(MOE_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return fail(MOE_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+  }
+  moe_graph* h = new (std::nothrow) moe_graph{g, ex};
+  if (!h) {
+    (void)hipGraphExecDestroy(ex);
+    (void)hipGraphDestroy(g);
+    return fail(MOE_ERR_INVALID_ARG, "out of host memory");
+  }
+  *graph = h;
+  return MOE_OK;
+}
+
+int moe_forward_graph_launch(moe_graph* graph, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!graph) return fail(MOE_ERR_INVALID_ARG, "graph is NULL");
+  const hipError_t e = hipGraphLaunch(graph->exec, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGraphLaunch: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int moe_forward_graph_destroy(moe_graph* graph) {
+  g_err[0] = 0;
+  if (!graph) return MOE_OK;
+  const hipError_t a = hipGraphExecDestroy(graph->exec);
+  const hipError_t b = hipGraphDestroy(graph->graph);
+  delete graph;
+  if (a != hipSuccess || b != hipSuccess)
+    return fail(MOE_ERR_HIP, "graph destroy: %s", hipGetErrorString(a != hipSuccess ? a : b));
+  return MOE_OK;
 }
 
 }  // extern "C"

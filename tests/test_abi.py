@@ -133,3 +133,50 @@ def test_workspace_sizes_grow_with_tokens(moe):
     # z for every padded routed row + the [T, k, H] expert output dominate
     cap, blocks = oracle.align_capacity(4096, 2, 8, 128)
     assert b >= blocks * 128 * 14336 * 2 + 4096 * 2 * 4096 * 2
+
+
+def test_batched_experts_validation_and_sizes(moe):
+    L = moe.binding.lib()
+    w = moe.MoeWeights()
+    w.num_experts, w.inter, w.quant, w.shared_inter = 8, 128, 0, 0
+    # negative max_tokens, missing weight pointers, workspace too small
+    assert L.moe_experts_batched(None, None, None, -1, 128, ctypes.byref(w), 0, 0, None, None, 0,
+                                 None) == 1
+    assert L.moe_experts_batched(None, None, None, 4, 128, ctypes.byref(w), 0, 0, None, None, 0,
+                                 None) == 1
+    w.w13 = w.w2 = 1
+    assert L.moe_experts_batched(1, None, 1, 4, 128, ctypes.byref(w), 0, 16, 1, None, 0, None) == 3
+    # M == 0 is a no-op before any pointer is read
+    assert L.moe_experts_batched(None, None, None, 0, 128, ctypes.byref(w), 0, 0, None, None, 0,
+                                 None) == 0
+    # fp8 caps block_m at 128; E * (M + block_m) is bounded
+    w.quant = 1
+    w.w13_scale = w.w2_scale = 1
+    assert L.moe_experts_batched(1, 1, 1, 4, 128, ctypes.byref(w), 0, 256, 1, None, 0, None) == 2
+    w.quant = 0
+    assert L.moe_experts_batched(1, None, 1, 1 << 28, 128, ctypes.byref(w), 0, 16, 1, None, 0,
+                                 None) == 1
+    # the workspace holds the schedule and z for E * ceil(M / bm) * bm rows
+    a = L.moe_experts_batched_workspace_bytes(16, 128, ctypes.byref(w), 0, 16)
+    b = L.moe_experts_batched_workspace_bytes(256, 128, ctypes.byref(w), 0, 16)
+    assert 0 < a < b
+    assert b >= 8 * 256 * (4 + 128 * 2)
+    lay = moe.moe_experts_batched_workspace_layout(100, 128, w, "silu", 32)
+    assert lay["rows"] == 8 * 4 * 32 and lay["sorted"] == 0 and lay["z"] >= lay["rows"] * 4
+    assert lay["z_scale"] is None
+
+
+def test_graph_entry_validation(moe):
+    L = moe.binding.lib()
+    w = moe.MoeWeights()
+    w.num_experts, w.inter, w.quant, w.shared_inter = 8, 128, 0, 0
+    null = None
+    h = ctypes.c_void_p()
+    args = [null, null, 4, 128, 2, 0, 1, 0, ctypes.byref(w), 0, 0, null, null, 1e-6, 0, null, null,
+            null, null, 0]
+    # no handle pointer; the null stream cannot be captured
+    assert L.moe_forward_graph_create(*args, 1, None) == 1
+    assert L.moe_forward_graph_create(*args, None, ctypes.byref(h)) == 1
+    assert not h.value
+    assert L.moe_forward_graph_destroy(None) == 0
+    assert L.moe_forward_graph_launch(None, None) == 1
