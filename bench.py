@@ -36,6 +36,8 @@ def parse():
                     help="family@T<tokens>, e.g. mixtral@T4096, deepseek_v3@T8192, llama4@T2048")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay leg (counter passes profile eager launches only)")
     ap.add_argument("--no-hbm-stages", action="store_true",
                     help="skip the finalize (hidden 7168) and align (2^24 ids) bandwidth legs")
     ap.add_argument("--cpu-sample", type=int, default=4096,
@@ -293,24 +295,26 @@ def main():
     # the same step replayed as one graph launch (moe_forward_graph_*): the
     # kernels and buffers are identical, only the per-kernel host submission
     # is gone -- the rate a decode loop sees
-    gstream = torch.cuda.Stream()
-    with torch.cuda.stream(gstream):
-        graph = moe.ForwardGraph(d["x"], d["logits"], w, spec.top_k, spec.scoring,
-                                 spec.renormalize, spec.apply_router_weight_on_input,
-                                 spec.activation, bm, d.get("residual"), d.get("gamma"), spec.eps,
-                                 spec.out_quant)
-        for _ in range(a.warmup):
+    graph_ms = None
+    if not a.no_graph:
+        gstream = torch.cuda.Stream()
+        with torch.cuda.stream(gstream):
+            graph = moe.ForwardGraph(d["x"], d["logits"], w, spec.top_k, spec.scoring,
+                                     spec.renormalize, spec.apply_router_weight_on_input,
+                                     spec.activation, bm, d.get("residual"), d.get("gamma"),
+                                     spec.eps, spec.out_quant)
+            for _ in range(a.warmup):
+                graph.launch(gstream)
+        torch.cuda.synchronize()
+        gstart, gstop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gstart.record(gstream)
+        for _ in range(a.steps):
             graph.launch(gstream)
-    torch.cuda.synchronize()
-    gstart, gstop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    gstart.record(gstream)
-    for _ in range(a.steps):
-        graph.launch(gstream)
-    gstop.record(gstream)
-    torch.cuda.synchronize()
-    graph_ms = gstart.elapsed_time(gstop) / a.steps
-    graph.close()
-    del graph
+        gstop.record(gstream)
+        torch.cuda.synchronize()
+        graph_ms = gstart.elapsed_time(gstop) / a.steps
+        graph.close()
+        del graph
     stage = {}
     for j in range(1, moe.NUM_STAGE_EVENTS):
         vals = [evs[i][j - 1].elapsed_time(evs[i][j]) for i in range(a.steps)]
@@ -348,8 +352,8 @@ def main():
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_TFLOPS[dtype], 4),
         "stage_ms": {k: round(v, 4) for k, v in stage.items()},
-        "graph": {"ms_per_step": round(graph_ms, 4),
-                  "tokens_per_s": round(spec.T / (graph_ms * 1e-3), 1)},
+        "graph": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 4), "tokens_per_s": round(spec.T / (graph_ms * 1e-3), 1)},
         "wall_s": round(wall, 3),
         "roofline": {"kernel": "routed GEMM-1 (gate+up, SiLU-mul fused)", "bound": "mfma",
                      "achieved": round(g1_tflops, 2), "peak": PEAK_TFLOPS[dtype],

@@ -117,4 +117,7 @@ PARITY_CASES = [
                  quant="fp8_token", shared_I=256, hot_experts=4, hot_fraction=0.05),
     WorkloadSpec("fp8_tensor_mini", 17, T=89, H=512, I=384, E=16, top_k=1, renormalize=False,
                  apply_router_weight_on_input=True, quant="fp8_tensor", shared_I=256),
+    # enough tokens for the shared expert's 256-row dense tiles (ragged: 1100 = 4*256 + 76)
+    WorkloadSpec("shared_dense_mini", 18, T=1100, H=512, I=256, E=8, top_k=2, shared_I=512,
+                 residual=True, rmsnorm=True),
 ]
