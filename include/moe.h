@@ -218,7 +218,7 @@ size_t moe_experts_workspace_bytes(int T, int H, int top_k, const moe_weights* w
  * so a caller can inspect what the second GEMM consumed.  out[5] receives
  * byte offsets from the workspace start (SIZE_MAX when absent):
  *   out[0] z of the routed rows, [rows, I] bf16 (E4M3 codes for fp8); row r
- *          belongs to flat row sorted_token_ids[r] (pad rows hold act(0))
+ *          belongs to flat row sorted_token_ids[r] (pad rows hold no data)
  *   out[1] its G(128) scales [rows, I/128] fp32 (fp8 only)
  *   out[2] z of the shared expert [T, I_s]   out[3] its scales (fp8 only)
  *   out[4] rows = block capacity * block_m (a count, not an offset)
@@ -346,7 +346,7 @@ int moe_forward_graph_destroy(moe_graph* graph);
 
 /* (host) the block_m moe_forward uses when given 0, by the average rows per
  * expert a = T*top_k/E: 16 (a <= 16), 32 (a <= 32), then bf16: 64 (a <= 64)
- * else 256; fp8: 64 (a <= 96) else 128.  quant is a moe_quant. */
+ * else 256; fp8: 64 (a <= 96), 128 (a <= 192) else 256.  quant is a moe_quant. */
 int moe_pick_block_m(int T, int top_k, int num_experts, int quant);
 
 #ifdef __cplusplus

@@ -3,8 +3,10 @@
 // Every tile is 128 output columns wide: on the first GEMM that is one
 // 128-column group of z, so the fused re-quantisation of z to E4M3 G(128)
 // finds each group's amax inside the tile.  BM 16/32 use 16x16x128 MFMA with
-// 4 waves split along N, BM 64/128 use 32x32x64 MFMA on 2x4 waves (two per
-// SIMD).
+// 4 waves split along N, BM 64/128/256 use 32x32x64 MFMA on 2x4 waves (two
+// per SIMD).  256-row tiles serve the second GEMM (and ungated first GEMMs):
+// the gated first GEMM would need a partial set beside 2 x 128 accumulators
+// per lane, which spills, so it runs two 128-row tiles per 256-row block.
 #include "gemm_impl.h"
 
 namespace moe {
@@ -15,7 +17,12 @@ static void dispatch_bm(int block_m, const GemmParams& p, int64_t max_mblk, hipS
     case 16: launch_gemm<GemmCfg<16, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s); break;
     case 32: launch_gemm<GemmCfg<32, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s); break;
     case 64: launch_gemm<GemmCfg<64, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s); break;
-    default: launch_gemm<GemmCfg<128, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s); break;
+    case 128: launch_gemm<GemmCfg<128, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s); break;
+    default:
+      // 256-row tiles exist for the ungated GEMMs only (a gated 256-row
+      // tile does not fit the registers); the host never asks for one
+      if constexpr (!GATED) launch_gemm<GemmCfg<256, 128, 2, 4, 32, true, false, AM, EP>>(p, max_mblk, s);
+      break;
   }
 }
 

@@ -420,6 +420,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       // scales; the latter are read ahead of the MFMAs unless registers are
       // held to 128 for occupancy (LEAN), then inside the promotion
       constexpr bool LEAN = gemm_min_waves_per_eu<C>() > 1;
+      constexpr bool PER_FRAGMENT = BM >= 256;
       const float swg[2] = {sW[kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
       const float* sAb = sA + (kt & 1) * BM;
       auto read_sa = [&](int fm, float (&out)[NACC]) {
@@ -430,13 +431,57 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
           for (int r = 0; r < 4; ++r) out[4 * q + r] = t[r];
         }
       };
-      float sa[LEAN ? 1 : FM][NACC];
-      if constexpr (!LEAN) {
+      float sa[(LEAN || PER_FRAGMENT) ? 1 : FM][NACC];
+      if constexpr (!LEAN && !PER_FRAGMENT) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) read_sa(fm, sa[fm]);
       }
       const uint8_t* As = smem + buf * STAGE;
       const uint8_t* Bs = As + A_BYTES;
+      if constexpr (PER_FRAGMENT) {
+        // 256-row tiles: each row fragment's partial is summed and promoted
+        // before the next one starts, so only one fragment's partial set is
+        // live beside the accumulators (a full partial set would double them).
+        frag_t fb[NSUB][G][FN];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              fb[s][g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          if (!(FULL || fm < fm_live)) continue;
+          acc_t pf[G][FN];
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s) {
+            const frag_t fa = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+              for (int fn = 0; fn < FN; ++fn) {
+                if (s == 0) {
+#pragma unroll
+                  for (int v = 0; v < NACC; ++v) pf[g][fn][v] = 0.f;
+                }
+                pf[g][fn] = M::mma(fa, fb[s][g][fn], pf[g][fn]);
+              }
+          }
+          float sr[NACC];
+          read_sa(fm, sr);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+              for (int v = 0; v < NACC; ++v)
+                acc[g][fm][fn][v] += pf[g][fn][v] * (sr[v] * swg[g]);
+        }
+        if (kt + 1 < nk && tid < BM) sA[((kt + 1) & 1) * BM + tid] = rsa;
+        buf ^= 1;
+        continue;
+      }
       acc_t part[G][FM][FN];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {

@@ -56,9 +56,11 @@ def test_pick_block_m(moe):
     assert moe.moe_pick_block_m(512, 2, 8) == 256
     assert moe.moe_pick_block_m(256, 2, 8) == 64
     assert moe.moe_pick_block_m(4096, 2, 8) == 256
-    assert moe.moe_pick_block_m(4096, 2, 8, "fp8") == 128
+    assert moe.moe_pick_block_m(4096, 2, 8, "fp8") == 256
+    assert moe.moe_pick_block_m(640, 2, 8, "fp8") == 128
     assert moe.moe_pick_block_m(64, 8, 256, "fp8") == 16
-    assert moe.moe_pick_block_m(8192, 8, 256, "fp8") == 128
+    assert moe.moe_pick_block_m(8192, 8, 256, "fp8") == 256
+    assert moe.moe_pick_block_m(4096, 8, 256, "fp8") == 128
 
 
 def test_align_workspace_is_zero_for_one_tile(moe):
@@ -113,11 +115,12 @@ def test_experts_validation(moe):
     # missing weight pointers
     assert L.moe_experts(None, None, None, None, 4, 128, 2, ctypes.byref(w), 0, None, None, None, 16,
                          None, None, None, 0, None) == 1
-    # fp8 experts cap block_m at 128
+    # fp8 takes every block_m (256-row blocks run the gated first GEMM as two
+    # 128-row tiles); a missing activation scale is an argument error
     w.quant = 1
     w.w13 = w.w2 = w.w13_scale = w.w2_scale = 1
-    assert L.moe_experts(None, None, None, None, 4, 128, 2, ctypes.byref(w), 0, None, None, None, 256,
-                         None, None, None, 0, None) == 2
+    assert L.moe_experts(1, None, None, None, 4, 128, 2, ctypes.byref(w), 0, 1, 1, 1, 256,
+                         1, None, None, 0, None) == 1
     # workspace too small
     w.quant = 0
     assert L.moe_experts(1, None, None, None, 4, 128, 2, ctypes.byref(w), 0, 1, 1, 1, 16,
@@ -149,10 +152,10 @@ def test_batched_experts_validation_and_sizes(moe):
     # M == 0 is a no-op before any pointer is read
     assert L.moe_experts_batched(None, None, None, 0, 128, ctypes.byref(w), 0, 0, None, None, 0,
                                  None) == 0
-    # fp8 caps block_m at 128; E * (M + block_m) is bounded
+    # fp8 at block_m 256 passes the checks up to the workspace; E * (M + block_m) is bounded
     w.quant = 1
     w.w13_scale = w.w2_scale = 1
-    assert L.moe_experts_batched(1, 1, 1, 4, 128, ctypes.byref(w), 0, 256, 1, None, 0, None) == 2
+    assert L.moe_experts_batched(1, 1, 1, 4, 128, ctypes.byref(w), 0, 256, 1, None, 0, None) == 3
     w.quant = 0
     assert L.moe_experts_batched(1, None, 1, 1 << 28, 128, ctypes.byref(w), 0, 16, 1, None, 0,
                                  None) == 1
