@@ -49,3 +49,23 @@ def test_golden_finalize_constant_row():
     out, _, _ = oracle.finalize(y, np.ones((1, 1), np.float32), False, shared=one, residual=one,
                                 gamma=gamma, eps=1e-6)
     assert np.all(out == g["out_bits"])
+
+
+def test_golden_prepare_per_token_and_tensor():
+    g = GOLD["prepare_fp8_per_token_and_tensor"]
+    x = np.concatenate([np.repeat(np.array(g["rows"], np.float64)[:, i:i + 1], 128, axis=1)
+                        for i in range(2)], axis=1)                       # [2, 256]
+    q, s = oracle.prepare(_bf16_bits(x), None, False, "fp8_token")
+    np.testing.assert_array_equal(s[:, 0], np.array(g["token_scales"], np.float32))
+    assert q[:, [0, 128]].tolist() == g["token_codes"]
+    assert np.all(q[:, :128] == q[:, :1]) and np.all(q[:, 128:] == q[:, 128:129])
+    q, s = oracle.prepare(_bf16_bits(x), None, False, "fp8_tensor")
+    assert s.shape == (1, 1) and s[0, 0] == np.float32(g["tensor_scale"])
+    assert q[:, [0, 128]].tolist() == g["tensor_codes"]
+
+
+def test_golden_experts_batched():
+    g = GOLD["experts_batched_hand"]
+    out = oracle.experts_batched(_bf16_bits(g["a"]), None, g["counts"], _bf16_bits(g["w13"]), None,
+                                 _bf16_bits(g["w2"]), None, "silu")
+    np.testing.assert_array_equal(out, _bf16_bits(g["out"]))
