@@ -222,21 +222,25 @@ def hbm_stages(torch, moe, dev):
     torch.cuda.empty_cache()
     sweep = []
     for E, kk, bm in ((8, 2, 256), (256, 8, 128)):
+        # four id sets with their outputs (4 x 128 MB > the last-level cache),
+        # called in rotation with preallocated outputs and workspace
         n = 1 << 24
         g = torch.Generator(device=dev)
         g.manual_seed(E)
-        ids = torch.randint(0, E, (n // kk, kk), device=dev, dtype=torch.int32, generator=g)
-        res = moe.moe_align(ids, E, bm)
+        idss = [torch.randint(0, E, (n // kk, kk), device=dev, dtype=torch.int32, generator=g)
+                for _ in range(4)]
+        ress = [moe.moe_align(ids, E, bm) for ids in idss]
 
-        def al(i, ids=ids, E=E, bm=bm):
-            moe.moe_align(ids, E, bm)
+        def al(i, idss=idss, ress=ress, E=E, bm=bm):
+            moe.moe_align(idss[i % 4], E, bm, out=ress[i % 4])
         us = timed(al, 20)
+        res = ress[0]
         alg = 4 * n + 4 * (res["sorted_token_ids"].numel() + res["block_expert_ids"].numel()) \
             + 8 * E + 8
         gbs = alg / us / 1e3
         sweep.append({"n_ids": n, "E": E, "top_k": kk, "block_m": bm, "us": round(us, 2),
                       "GB_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
-        del ids, res
+        del idss, ress, res
     out["align_sweep"] = sweep
     return out
 

@@ -177,11 +177,10 @@ int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
 int moe_align_capacity(int T, int top_k, int E, int block_m,
                        int64_t* sorted_capacity, int64_t* block_capacity);
 /* (host) workspace moe_align needs: 0 for T*top_k <= 32768 ids; above that,
- * 4*E*(4*tiles + ceil(4*tiles/64)) bytes (per-expert counts of each quarter
- * tile, and of blocks of 64 of them), where tiles = ceil(T*top_k / tile) and
- * tile is the smallest power of two in [2048, 65536] that gives at most 2048
- * tiles and, unless that would leave fewer than 512 tiles, holds at least
- * 128*E ids. */
+ * 4*E*(9*tiles + 1) bytes (per-expert counts of each eighth of a tile, the
+ * tiles' per-expert totals and the expert totals), where tiles =
+ * ceil(T*top_k / tile) and tile is the smallest power of two in
+ * [2048, 8192] with tile*1024 >= T*top_k (8192 above 2^23 ids). */
 size_t moe_align_workspace_bytes(int T, int top_k, int E, int block_m);
 
 /*

@@ -194,19 +194,24 @@ def moe_prepare(a1, topk_weights, apply_router_weight_on_input=False, quant="non
     return a1q, (a1q_scale if _is_fp8(quant) else None)
 
 
-def moe_align(topk_ids, E, block_m, stream=None):
+def moe_align(topk_ids, E, block_m, stream=None, out=None, workspace=None):
+    """Returns a dict of the align outputs; ``out`` (such a dict from an
+    earlier call of the same shape) and ``workspace`` are reused when given."""
     T, k = topk_ids.shape
     dev = topk_ids.device
-    scap, bcap = moe_align_capacity(T, k, E, block_m)
-    out = {
-        "expert_counts": torch.empty(E, dtype=torch.int32, device=dev),
-        "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-        "sorted_token_ids": torch.empty(scap, dtype=torch.int32, device=dev),
-        "block_expert_ids": torch.empty(bcap, dtype=torch.int32, device=dev),
-        "num_tokens_post_padded": torch.empty(1, dtype=torch.int32, device=dev),
-    }
+    if out is None:
+        scap, bcap = moe_align_capacity(T, k, E, block_m)
+        out = {
+            "expert_counts": torch.empty(E, dtype=torch.int32, device=dev),
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "sorted_token_ids": torch.empty(scap, dtype=torch.int32, device=dev),
+            "block_expert_ids": torch.empty(bcap, dtype=torch.int32, device=dev),
+            "num_tokens_post_padded": torch.empty(1, dtype=torch.int32, device=dev),
+        }
     wsb = _lib.moe_align_workspace_bytes(T, k, E, block_m)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ws = workspace if workspace is not None else out.get("_ws")
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     _check(_lib.moe_align(_ptr(topk_ids), T, k, E, block_m, _ptr(out["expert_counts"]),
                           _ptr(out["expert_offsets"]), _ptr(out["sorted_token_ids"]),
                           _ptr(out["block_expert_ids"]), _ptr(out["num_tokens_post_padded"]),

@@ -67,12 +67,14 @@ def test_align_workspace_is_zero_for_one_tile(moe):
     lib = moe.binding.lib()
     assert lib.moe_align_workspace_bytes(16, 2, 8, 16) == 0
     assert lib.moe_align_workspace_bytes(4096, 8, 256, 16) == 0          # 32768 ids: one workgroup
-    # 65536 ids: 32 tiles of 2048 = 128 quarter tiles, 2 scan blocks of 64
-    assert lib.moe_align_workspace_bytes(8192, 8, 256, 16) == (128 + 2) * 256 * 4
-    # 2^24 ids, E=256: 512 tiles of 32768 (>= 128 ids per expert) = 2048 quarter tiles
-    assert lib.moe_align_workspace_bytes(1 << 21, 8, 256, 128) == (2048 + 32) * 256 * 4
-    # 2^24 ids, E=8: 2048 tiles of 8192 = 8192 quarter tiles, 128 scan blocks
-    assert lib.moe_align_workspace_bytes(1 << 23, 2, 8, 256) == (8192 + 128) * 8 * 4
+    # 65536 ids: 32 tiles of 2048 (8 wave counts + 1 tile total per tile and expert)
+    assert lib.moe_align_workspace_bytes(8192, 8, 256, 16) == (32 * 9 + 1) * 256 * 4
+    # 2^24 ids: 2048 tiles of 8192 (the LDS-sized maximum)
+    assert lib.moe_align_workspace_bytes(1 << 21, 8, 256, 128) == (2048 * 9 + 1) * 256 * 4
+    assert lib.moe_align_workspace_bytes(1 << 23, 2, 8, 256) == (2048 * 9 + 1) * 8 * 4
+    # 2^20 ids: 512 tiles of 2048; 2^22: 1024 of 4096
+    assert lib.moe_align_workspace_bytes(1 << 17, 8, 64, 64) == (512 * 9 + 1) * 64 * 4
+    assert lib.moe_align_workspace_bytes(1 << 21, 2, 8, 256) == (1024 * 9 + 1) * 8 * 4
 
 
 def _bad(moe, fn, *args):

@@ -170,10 +170,14 @@ def test_align_adversarial(T, k, E, BM, pattern):
 
 
 @pytest.mark.parametrize("T,k,E,BM", [(20000, 8, 256, 128), (200000, 8, 256, 128),
-                                      (600000, 8, 64, 64), (2100000, 2, 8, 256)])
+                                      (600000, 8, 64, 64), (2100000, 2, 8, 256),
+                                      (2100001, 8, 256, 128), (600000, 4, 1024, 128),
+                                      (300000, 1, 3, 16)])
 def test_align_multi_tile_sizes(T, k, E, BM):
-    """Enough ids for several first-level scan blocks (over 64 tiles) and for
-    tiles above the 2048-id minimum."""
+    """Every tile size from the 2048-id minimum to the 8192-id maximum (over
+    2^23 ids), tile counts that are not a multiple of the 8 XCDs, the column
+    scan over more tiles than one pass of its workgroup, E up to 1024 (the
+    larger LDS sizing of the scatter), a ragged last tile."""
     _announce(f"align large T={T} k={k} E={E} BM={BM}")
     g = torch.Generator().manual_seed(T + E)
     ids = torch.rand((T, E), generator=g).argsort(dim=1)[:, :k].to(torch.int32).contiguous()
