@@ -244,10 +244,19 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   // (sW: gate row, then up row).  bf16 tiles use every byte of the 160 KB
   // for stages.
   constexpr int kMaxKB = 128;  // K <= 16384
-  constexpr int SCALE_BYTES = FP8 ? (2 * BM + 2 * kMaxKB) * 4 : 0;
+  // Activation scales: the tile's whole table [k-tile][row] when its k-tiles
+  // fit SA_KB (loaded once before the k-loop), else two k-tiles in turn.
+  // SA_KB (2..64) takes what the LDS leaves without lowering the number of
+  // workgroups per CU that the tile had with two k-tiles of scales.
+  constexpr int kLds = 163840;
+  constexpr int BASE_BYTES = SMEM_TILE + (2 * BM + 2 * kMaxKB) * 4;
+  constexpr int PER_WG = kLds / (kLds / BASE_BYTES);
+  constexpr int SA_FIT = (PER_WG - SMEM_TILE - 2 * kMaxKB * 4) / (BM * 4);
+  constexpr int SA_KB = !FP8 ? 2 : (SA_FIT < 2 ? 2 : (SA_FIT > 64 ? 64 : SA_FIT));
+  constexpr int SCALE_BYTES = FP8 ? (SA_KB * BM + 2 * kMaxKB) * 4 : 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_TILE + SCALE_BYTES];
   float* const sA = reinterpret_cast<float*>(smem + SMEM_TILE);
-  float* const sW = sA + 2 * BM;
+  float* const sW = sA + SA_KB * BM;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -400,20 +409,79 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   // acc += partial * s_a[row] * s_w.  The k-tile's activation scales are
   // read from LDS (16-byte reads: an accumulator's rows come in runs of 4)
   // right after the barrier, so their latency hides behind the MFMAs.
+  // The rows' scales reach LDS by direct-to-LDS loads issued with the
+  // k-tile's stage loads, so the loop's one vmcnt(0) covers them.  (Loaded
+  // into a register and stored to LDS at the end of the iteration, each
+  // such load made the compiler wait for vmcnt(0) inside the iteration --
+  // loads complete in order -- which also drained the next k-tile's stage
+  // loads: 12 % of the gated first GEMM's time at DeepSeek-V3 T=8192.)
   // (Deferring each promotion by one k-tile with two partial sets was
   // measured slower: the extra registers cost occupancy.)
   auto kloop_fp8 = [&](auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     static_assert(!FP8 || NSTAGE == 2, "fp8 runs two LDS stages");
-    if (tid < BM) sA[tid] = p.a_scale[static_cast<int64_t>(a_srow) * p.sa_row + kbase * p.sa_k];
-    if (nk > 0) dma(0, 0);
+    // Whole table: thread r < BM loads its row's scales of this tile's
+    // k-tiles (16-byte loads where the row's G(128) scales are contiguous and
+    // aligned) and stores them to sA[kt][r]; the first barrier publishes
+    // them.  The loads are consumed here, before the loop, so none is in
+    // flight into a register when it starts.
+    const bool whole = nk <= SA_KB;
+    // Otherwise row r's scale of k-tile kt goes straight to sA[kt & 1][r] by
+    // a 4-byte direct-to-LDS load (threads r < BM; lane i of a wave writes 4*i
+    // bytes past the wave's base), issued with the k-tile's stage loads.
+    auto dma_sa = [&](int kt, int b) {
+      if (tid < BM) {
+        typedef __attribute__((address_space(3))) void lds_void;
+        const float* g = p.a_scale + static_cast<int64_t>(a_srow) * p.sa_row +
+                         static_cast<int64_t>(kbase + kt) * p.sa_k;
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(sA + b * BM + (tid & ~63)), 4, 0, 0);
+      }
+    };
+    if (nk > 0) {
+      if (!whole) dma_sa(0, 0);
+      dma(0, 0);
+    }
+    if (whole && tid < BM) {
+      // batches of up to 8 loads in flight before their stores (the first
+      // k-tile's stage loads are already under way)
+      const float* g = p.a_scale + static_cast<int64_t>(a_srow) * p.sa_row +
+                       static_cast<int64_t>(kbase) * p.sa_k;
+      int kv = 0;   // scales taken by whole 16-byte loads (never past k-tile nk-1)
+      if (p.sa_k == 1 && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+        kv = nk & ~3;
+        for (int k0 = 0; k0 < kv; k0 += 32) {
+          f32x4 v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (k0 + 4 * j < kv) v[j] = *reinterpret_cast<const f32x4*>(g + k0 + 4 * j);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (k0 + 4 * j < kv) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sA[(k0 + 4 * j + i) * BM + tid] = v[j][i];
+            }
+        }
+      }
+      {
+        for (int k0 = kv; k0 < nk; k0 += 8) {
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (k0 + j < nk) v[j] = g[static_cast<int64_t>(k0 + j) * p.sa_k];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (k0 + j < nk) sA[(k0 + j) * BM + tid] = v[j];
+        }
+      }
+    }
     int buf = 0;
     for (int kt = 0; kt < nk; ++kt) {
+      // k-tile kt's loads (stage and scales) have landed
       wait_vm_loads();
       lds_barrier();
-      float rsa = 0.f;
       if (kt + 1 < nk) {
-        if (tid < BM) rsa = p.a_scale[static_cast<int64_t>(a_srow) * p.sa_row + (kbase + kt + 1) * p.sa_k];
+        // buffer (kt+1)&1 was last read in iteration kt-1, before this barrier
+        if (!whole) dma_sa(kt + 1, (kt + 1) & 1);
         dma(kt + 1, buf ^ 1);
       }
       // this k-tile's scales: weight blocks (gate, up) and the rows' activation
@@ -422,7 +490,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       constexpr bool LEAN = gemm_min_waves_per_eu<C>() > 1;
       constexpr bool PER_FRAGMENT = BM >= 256;
       const float swg[2] = {sW[kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
-      const float* sAb = sA + (kt & 1) * BM;
+      const float* sAb = sA + (whole ? kt : (kt & 1)) * BM;
       auto read_sa = [&](int fm, float (&out)[NACC]) {
 #pragma unroll
         for (int q = 0; q < NACC / 4; ++q) {
@@ -478,7 +546,6 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
               for (int v = 0; v < NACC; ++v)
                 acc[g][fm][fn][v] += pf[g][fn][v] * (sr[v] * swg[g]);
         }
-        if (kt + 1 < nk && tid < BM) sA[((kt + 1) & 1) * BM + tid] = rsa;
         buf ^= 1;
         continue;
       }
@@ -527,7 +594,6 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
             for (int v = 0; v < NACC; ++v)
               acc[g][fm][fn][v] += part[g][fm][fn][v] * (sr[v] * swg[g]);
       }
-      if (kt + 1 < nk && tid < BM) sA[((kt + 1) & 1) * BM + tid] = rsa;
       buf ^= 1;
     }
   };
