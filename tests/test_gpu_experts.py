@@ -59,6 +59,24 @@ def _path(spec):
 @pytest.mark.parametrize("spec", PARITY_CASES, ids=lambda s: s.name)
 @pytest.mark.parametrize("BM", [16, 64, 128, 256])
 def test_experts_stage_reduced(spec, BM):
+    _experts_case(spec, BM)
+
+
+# K long enough that an fp8 tile's activation-scale table does not fit the
+# LDS the tile leaves free: H = 8320 (65 k-tiles) for the gated first GEMM and
+# the shared expert's (capacity 64), I = 3968 (31 k-tiles) for the second GEMM
+# at 64 and 128 rows (capacities 17 and 30).  Those launches take the
+# per-k-tile direct-to-LDS scale loads instead of the whole table.
+FP8_LONG_K = WorkloadSpec("fp8_long_k", 19, T=37, H=8320, I=3968, E=2, top_k=2,
+                          scoring="sigmoid", quant="fp8", shared_I=3968)
+
+
+@pytest.mark.parametrize("BM", [64, 128])
+def test_experts_fp8_long_k_scale_loads(BM):
+    _experts_case(FP8_LONG_K, BM)
+
+
+def _experts_case(spec, BM):
     _announce(f"experts {spec.name} BM={BM}")
     moe = _moe()
     d = make_layer_inputs(spec)
