@@ -74,8 +74,12 @@ void launch_gemm_bf16(int kind, bool gated, int block_m, int bnz, const GemmPara
 }
 
 int gemm_tile_n(int kind, bool fp8, bool gated, int block_m, int n) {
-  if (fp8) return 128;
   const bool first = kind == GEMM_Z_ROUTED || kind == GEMM_Z_DENSE;
+  // fp8: 128 columns (a z group on the first GEMM); second GEMMs of 16 or 32
+  // rows take 256 (half the tiles, each re-reading its z rows half as often;
+  // still two workgroups per CU -- at 64 rows the wider tile would hold a CU
+  // alone, and measured slower)
+  if (fp8) return (!first && block_m <= 32 && n % 256 == 0) ? 256 : 128;
   if (first && gated) return (block_m >= 128 && n % 128 == 0) ? 128 : 64;
   if (first) return 128;
   return (block_m == 256 && n % 256 == 0) ? 256 : 128;

@@ -260,6 +260,12 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  // fp8, ungated, 256 columns: each wave's columns lie in one of the tile's
+  // two 128-row weight-scale blocks, wblk
+  constexpr bool WIDE = FP8 && !C::GATED && BNZ > 128;
+  static_assert(!FP8 || (C::GATED ? BNZ == 128 : (BNZ == 128 || (BNZ == 256 && 128 % WN == 0))),
+                "fp8 tiles: 128 columns, or 256 ungated with each wave inside one scale block");
+  const int wblk = WIDE ? (wn * WN) / 128 : 0;
 
   // ---- tile decode (XCD-aware grouped order) ----
   // split K: the grid holds ksplit copies of the tile grid, split-major
@@ -368,9 +374,12 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
     }
     sw_row0 = wsbase + static_cast<int64_t>(n0 / 128) * kblocks;
     if constexpr (C::GATED) sw_row1 = wsbase + static_cast<int64_t>((p.inter + n0) / 128) * kblocks;
+    // an ungated tile 256 columns wide spans two 128-row weight blocks: the
+    // second one's scales take the slot the up half uses in a gated tile
+    if constexpr (WIDE) sw_row1 = wsbase + static_cast<int64_t>(n0 / 128 + 1) * kblocks;
     for (int i = tid; i < kblocks; i += NT) {
       sW[i] = sw_row0[i];
-      if constexpr (C::GATED) sW[kMaxKB + i] = sw_row1[i];
+      if constexpr (C::GATED || WIDE) sW[kMaxKB + i] = sw_row1[i];
     }
     // made visible by the first k-tile's barrier
   }
@@ -489,7 +498,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       // held to 128 for occupancy (LEAN), then inside the promotion
       constexpr bool LEAN = gemm_min_waves_per_eu<C>() > 1;
       constexpr bool PER_FRAGMENT = BM >= 256;
-      const float swg[2] = {sW[kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
+      const float swg[2] = {sW[wblk * kMaxKB + kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
       const float* sAb = sA + (whole ? kt : (kt & 1)) * BM;
       auto read_sa = [&](int fm, float (&out)[NACC]) {
 #pragma unroll
