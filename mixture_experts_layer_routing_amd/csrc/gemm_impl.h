@@ -387,12 +387,22 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   // this workgroup's k-tiles: [kbase, kbase + nk)
   const int nk = p.K / (RB / EB) / p.ksplit;
   const int kbase = ks * nk;
-  auto dma = [&](int kt, int buf) {
+  // In the k-loop of tiles with padding rows (not FULL), load groups of A
+  // rows that lie wholly past the block's data rows (the padding at the end
+  // of an expert's segment, or past T) are not loaded: their LDS rows keep
+  // stale values, which only ever reach the outputs of pad rows (MFMA rows
+  // are independent), and those are never stored or read.  A half-filled
+  // 256-row block saves a quarter of its loads.  The count of loads in
+  // flight then varies by wave, so this needs the two-stage loop, which
+  // waits for all of them (vmcnt(0)).  Full tiles keep branch-free loads.
+  const int a_groups = (NSTAGE == 2) ? (valid_rows + RPG - 1) / RPG : BM / RPG;
+  auto dma = [&](int kt, int buf, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     kt += kbase;
 #pragma unroll
     for (int s = 0; s < NIW; ++s) {
       const int j = wave + NW * s;
-      if (NI % NW == 0 || j < NI)
+      if ((NI % NW == 0 || j < NI) && (FULL || j >= BM / RPG || j < a_groups))
         lds_dma16(src[s] + static_cast<int64_t>(kt) * RB, smem + buf * STAGE + j * 1024);
     }
   };
@@ -448,7 +458,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
     };
     if (nk > 0) {
       if (!whole) dma_sa(0, 0);
-      dma(0, 0);
+      dma(0, 0, full_tag);
     }
     if (whole && tid < BM) {
       // batches of up to 8 loads in flight before their stores (the first
@@ -491,7 +501,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       if (kt + 1 < nk) {
         // buffer (kt+1)&1 was last read in iteration kt-1, before this barrier
         if (!whole) dma_sa(kt + 1, (kt + 1) & 1);
-        dma(kt + 1, buf ^ 1);
+        dma(kt + 1, buf ^ 1, full_tag);
       }
       // this k-tile's scales: weight blocks (gate, up) and the rows' activation
       // scales; the latter are read ahead of the MFMAs unless registers are
@@ -618,7 +628,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
     }
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st)
-      if (st < nk) dma(st, st);
+      if (st < nk) dma(st, st, full_tag);
     int buf = 0;                       // kt % NSTAGE
     int nbuf = NSTAGE - 1;             // (kt + NSTAGE - 1) % NSTAGE
     for (int kt = 0; kt < nk; ++kt) {
@@ -631,7 +641,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
         wait_vm_loads();
       }
       lds_barrier();
-      if (kt + NSTAGE - 1 < nk) dma(kt + NSTAGE - 1, nbuf);
+      if (kt + NSTAGE - 1 < nk) dma(kt + NSTAGE - 1, nbuf, full_tag);
       const uint8_t* As = smem + buf * STAGE;
       const uint8_t* Bs = As + A_BYTES;
       {
