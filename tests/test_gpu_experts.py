@@ -76,6 +76,39 @@ def test_experts_fp8_long_k_scale_loads(BM):
     _experts_case(FP8_LONG_K, BM)
 
 
+@pytest.mark.parametrize("name", ["mixtral_mini", "deepseek_mini", "decode_split_fp8_mini"])
+@pytest.mark.parametrize("BM", [64, 256])
+def test_experts_outputs_ignore_padding_and_workspace_contents(name, BM):
+    """Tiles with padding rows skip loading those rows and compute them on
+    stale LDS; split-K partials and z cover only data rows.  So the outputs
+    must not depend on anything but data rows: a workspace filled with 0xFF
+    bytes (NaN in every float format) gives the same bits as a zeroed one."""
+    spec = next(s for s in PARITY_CASES if s.name == name)
+    _announce(f"experts padding/workspace independence {name} BM={BM}")
+    moe = _moe()
+    d = make_layer_inputs(spec)
+    dd = {k: v.to(DEV) for k, v in d.items()}
+    rid, rw = oracle.route(d["logits"].numpy(), spec.top_k, spec.scoring, spec.renormalize)
+    ids = torch.from_numpy(rid).to(DEV)
+    tw = torch.from_numpy(rw).to(DEV)
+    a1q, a1s = moe.moe_prepare(dd["x"], tw, spec.apply_router_weight_on_input, spec.quant)
+    al = moe.moe_align(ids, spec.E, BM)
+    w = _weights(moe, dd, spec.quant)
+    nbytes = moe.binding.lib().moe_experts_workspace_bytes(
+        spec.T, spec.H, spec.top_k, moe.binding.ctypes.byref(w),
+        moe.binding.ACTIVATION[spec.activation], BM)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((max(nbytes, 1),), fill, dtype=torch.uint8, device=DEV)
+        feo, sho = moe.moe_experts(a1q, a1s, w, spec.top_k, al, BM, spec.activation, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((feo.clone(), None if sho is None else sho.clone()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    if outs[0][1] is not None:
+        assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+    assert torch.isfinite(outs[1][0].float()).all()
+
+
 def _experts_case(spec, BM):
     _announce(f"experts {spec.name} BM={BM}")
     moe = _moe()
