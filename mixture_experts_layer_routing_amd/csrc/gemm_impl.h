@@ -428,12 +428,14 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   // acc += partial * s_a[row] * s_w.  The k-tile's activation scales are
   // read from LDS (16-byte reads: an accumulator's rows come in runs of 4)
   // right after the barrier, so their latency hides behind the MFMAs.
-  // The rows' scales reach LDS by direct-to-LDS loads issued with the
-  // k-tile's stage loads, so the loop's one vmcnt(0) covers them.  (Loaded
-  // into a register and stored to LDS at the end of the iteration, each
-  // such load made the compiler wait for vmcnt(0) inside the iteration --
-  // loads complete in order -- which also drained the next k-tile's stage
-  // loads: 12 % of the gated first GEMM's time at DeepSeek-V3 T=8192.)
+  // The rows' scales reach LDS as one [k-tile][row] table per tile, loaded
+  // before the loop; when the table does not fit, by a direct-to-LDS load
+  // per k-tile issued with the stage loads.  Either way no load into a
+  // register is in flight inside the loop.  (Loaded into a register and
+  // stored to LDS at the end of each iteration, the scale made the compiler
+  // wait for vmcnt(0) inside the iteration -- loads complete in order --
+  // which also drained the next k-tile's stage loads: 12 % of the gated
+  // first GEMM's time at DeepSeek-V3 T=8192.)
   // (Deferring each promotion by one k-tile with two partial sets was
   // measured slower: the extra registers cost occupancy.)
   auto kloop_fp8 = [&](auto full_tag) {
