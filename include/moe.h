@@ -136,9 +136,30 @@ int moe_route(const float* logits, int T, int E, int top_k, int scoring, int ren
               int32_t* topk_ids, float* topk_weights, hipStream_t stream);
 
 /*
- * moe_prepare -- the no-DP/EP prepare ("[vLLM] MoE Oracle & Prepare/Finalize"):
- * if apply_router_weight_on_input, top_k must be 1 (else MOE_ERR_INVALID_ARG,
- * the page's assert) and a = bf16(a1 * bf16(topk_weights)); then quantise:
+ * The quant_config of the pages' prepare contract ("[vLLM] MoE Oracle &
+ * Prepare/Finalize", no-DP/EP prepare code): which activation format
+ * prepare emits and the weight block grid the experts expect with it.
+ *   quant      a moe_quant
+ *   act_group  activation channels per scale: 128 with MOE_QUANT_FP8_G128;
+ *              0 with MOE_QUANT_FP8_TOKEN and MOE_QUANT_FP8_TENSOR (the
+ *              group is the row, or the whole tensor); ignored with NONE
+ *   w_block_n, w_block_k  weight-scale block (rows, columns): 128, 128 with
+ *              every fp8 format; ignored with NONE
+ * Any other group or block size is MOE_ERR_UNSUPPORTED.
+ */
+typedef struct moe_quant_config {
+  int32_t quant;
+  int32_t act_group;
+  int32_t w_block_n;
+  int32_t w_block_k;
+} moe_quant_config;
+
+/*
+ * moe_prepare -- the no-DP/EP prepare ("[vLLM] MoE Oracle & Prepare/Finalize",
+ * the no-DP/EP prepare code: prepare(a1, topk_weights, topk_ids, ...,
+ * apply_router_weight_on_input, quant_config)): if apply_router_weight_on_input,
+ * top_k must be 1 (else MOE_ERR_INVALID_ARG, the page's assert) and
+ * a = bf16(a1 * bf16(topk_weights)); then quantise per qc->quant:
  *   MOE_QUANT_NONE:     a1q [T, H] bf16 = a        (a1q_scale unused, may be NULL)
  *   MOE_QUANT_FP8_G128: per (t, g): s = max(amax, 1e-10) / 448 (fp32),
  *                       q = E4M3_rne_sat(a / s);   a1q [T, H] E4M3, a1q_scale [T, H/128] fp32
@@ -146,16 +167,24 @@ int moe_route(const float* logits, int T, int E, int top_k, int scoring, int ren
  *   MOE_QUANT_FP8_TENSOR: the same rule with amax over all of a; a1q_scale [1]
  *   a1             [T, H] bf16
  *   topk_weights   [T, top_k] fp32 (read only when apply_router_weight_on_input)
- * Limits: H % 8 == 0; H % 128 == 0 for fp8.  a1q may alias a1 only for
- * MOE_QUANT_NONE.
+ *   topk_ids       [T, top_k] int32, accepted for the pages' signature and not
+ *                  read: without expert parallelism there is no dispatch, so
+ *                  the ids pass through unchanged (may be NULL)
+ *   qc             (host) the quant config above; NULL is MOE_ERR_INVALID_ARG
+ * Limits: H % 8 == 0; H % 128 == 0 for fp8; H <= 16384 per token.  a1q may
+ * alias a1 only for MOE_QUANT_NONE.
  */
-int moe_prepare(const uint16_t* a1, int T, int H, const float* topk_weights, int top_k,
-                int apply_router_weight_on_input, int quant, void* a1q, float* a1q_scale,
+int moe_prepare(const uint16_t* a1, int T, int H, const float* topk_weights,
+                const int32_t* topk_ids, int top_k, int apply_router_weight_on_input,
+                const moe_quant_config* qc /* host */, void* a1q, float* a1q_scale,
                 hipStream_t stream);
 
 /*
  * moe_align -- sort the T*top_k flat rows i = t*top_k + j by expert into
- * block_m-padded groups (deterministic; only one result is correct):
+ * block_m-padded groups.  Not a step the pages define: they hand topk_ids
+ * to the experts and say only that each expert computes on its own tokens
+ * ("Fused MoE Kernel Features", fused experts section); this is the plain
+ * reading, a stable counting sort (deterministic; only one result is correct):
  *   expert_counts[e]   = #{i : ids[i] == e}                                  [E]
  *   expert_offsets[0]  = 0, [e+1] = [e] + ceil(counts[e] / block_m) * block_m  [E+1]
  *   sorted_token_ids   = per expert, its flat rows in ascending order, then
@@ -198,7 +227,8 @@ size_t moe_align_workspace_bytes(int T, int top_k, int E, int block_m);
  *   sorted_token_ids, block_expert_ids, num_tokens_post_padded: moe_align's
  *                       output for the same topk_ids and block_m
  *   workspace           moe_experts_workspace_bytes bytes
- * Limits: H % 64 == 0 and I % 64 == 0 (bf16), H % 128 == 0 and I % 128 == 0 (fp8);
+ * Limits: H % 128 == 0 (the second GEMM writes 128-column tiles); I % 64 == 0
+ * for the gated bf16 activations, I % 128 == 0 otherwise; H, I <= 16384;
  * weights->quant must equal the activation format.
  */
 int moe_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
@@ -227,8 +257,8 @@ int moe_experts_workspace_layout(int T, int H, int top_k, const moe_weights* wei
 
 /*
  * moe_experts_batched -- the experts stage on the batched activation format
- * ("Fused MoE Modular Kernel" / "Fused MoE Kernel Features": prepare emits
- * either the standard or the batched format, and the batched experts
+ * ("Fused MoE Kernel Features", backend and fused experts sections: prepare
+ * emits either the standard or the batched format, and the batched experts
  * kernels take one batch of rows per expert).  With M = max_tokens, rows
  * [0, expert_num_tokens[e]) of batch e are expert e's input; for each such
  * row m
@@ -294,7 +324,12 @@ int moe_finalize(void* output, float* output_scale, int out_quant,
 /*
  * moe_forward -- the whole layer, enqueued on one stream with no host sync:
  * route -> prepare -> align -> experts (routed GEMM-1, GEMM-2, shared expert)
- * -> finalize, intermediates in `workspace`.
+ * -> finalize, intermediates in `workspace`.  The pages describe the stages
+ * one by one ("[vLLM] MoE Oracle & Prepare/Finalize": the modular kernel runs
+ * prepare, the experts and finalize in turn); this call is their composition
+ * in that order, with routing (not on the pages) in front, and it takes the
+ * same readings as the stage calls above.  The activation format is
+ * weights->quant with the fixed 128 group and 128x128 weight blocks.
  *   x [T, H] bf16; logits [T, E] fp32; weights (host struct) as moe_experts;
  *   block_m 0 = choose (moe_pick_block_m); residual/gamma/residual_out as
  *   moe_finalize; output/output_scale per out_quant.

@@ -8,7 +8,9 @@ raises ImportError when the library has not been built.
 from .binding import (  # noqa: F401
     ForwardGraph,
     MoeError,
+    MoeQuantConfig,
     MoeWeights,
+    quant_config,
     make_weights,
     moe_align,
     moe_align_capacity,

@@ -47,6 +47,18 @@ class MoeWeights(ctypes.Structure):
                 ("shared_w2_scale", c_vp)]
 
 
+class MoeQuantConfig(ctypes.Structure):
+    _fields_ = [("quant", c_i32), ("act_group", c_i32), ("w_block_n", c_i32), ("w_block_k", c_i32)]
+
+
+def quant_config(quant="none", act_group=None, w_block_n=128, w_block_k=128):
+    """The prepare quant_config: the format, its activation group (128 for
+    G(128), 0 for per token / per tensor) and the 128x128 weight blocks."""
+    if act_group is None:
+        act_group = 128 if quant == "fp8" else 0
+    return MoeQuantConfig(QUANT[quant], act_group, w_block_n, w_block_k)
+
+
 class MoeError(RuntimeError):
     def __init__(self, status, fn, msg):
         super().__init__(f"{fn} -> {status_str(status)}: {msg}")
@@ -63,7 +75,8 @@ def _load():
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_pick_block_m": (c_int, [c_int, c_int, c_int, c_int]),
         "moe_route": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
-        "moe_prepare": (c_int, [c_vp, c_int, c_int, c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
+        "moe_prepare": (c_int, [c_vp, c_int, c_int, c_vp, c_vp, c_int, c_int,
+                                ctypes.POINTER(MoeQuantConfig), c_vp, c_vp, c_vp]),
         "moe_align": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
                               c_vp, c_sz, c_vp]),
         "moe_align_capacity": (c_int, [c_int, c_int, c_int, c_int, ctypes.POINTER(c_i64),
@@ -178,18 +191,25 @@ def moe_route(logits, top_k, scoring="softmax", renormalize=True, topk_ids=None,
     return topk_ids, topk_weights
 
 
-def moe_prepare(a1, topk_weights, apply_router_weight_on_input=False, quant="none",
-                a1q=None, a1q_scale=None, stream=None):
+def moe_prepare(a1, topk_weights=None, topk_ids=None, apply_router_weight_on_input=False,
+                quant="none", a1q=None, a1q_scale=None, stream=None, qc=None):
+    """prepare(a1, topk_weights, topk_ids, apply_router_weight_on_input,
+    quant_config) -> (a1q, a1q_scale or None).  ``qc`` (a MoeQuantConfig)
+    overrides the config built from ``quant``; ``topk_ids`` is passed through
+    to the library, which does not read it without expert parallelism."""
     T, H = a1.shape
     dev = a1.device
-    top_k = 1 if topk_weights is None else topk_weights.shape[1]
+    qc = quant_config(quant) if qc is None else qc
+    quant = {v: k for k, v in QUANT.items()}.get(qc.quant, quant)
+    top_k = (topk_weights.shape[1] if topk_weights is not None
+             else (topk_ids.shape[1] if topk_ids is not None else 1))
     if a1q is None:
         a1q = torch.empty((T, H), dtype=torch.uint8 if _is_fp8(quant) else torch.bfloat16,
                           device=dev)
     if _is_fp8(quant) and a1q_scale is None:
         a1q_scale = torch.empty(_act_scale_shape(quant, T, H), dtype=torch.float32, device=dev)
-    _check(_lib.moe_prepare(_ptr(a1), T, H, _ptr(topk_weights), top_k,
-                            int(apply_router_weight_on_input), QUANT[quant], _ptr(a1q),
+    _check(_lib.moe_prepare(_ptr(a1), T, H, _ptr(topk_weights), _ptr(topk_ids), top_k,
+                            int(apply_router_weight_on_input), ctypes.byref(qc), _ptr(a1q),
                             _ptr(a1q_scale), _stream(stream)), "moe_prepare")
     return a1q, (a1q_scale if _is_fp8(quant) else None)
 

@@ -31,45 +31,57 @@ template <int BM, int BNZ, int WM, int WN, int MF, bool GATED, int AM, int EP>
 using Bf16Cfg = GemmCfg<BM, BNZ, WM, WN, MF, false, GATED, AM, EP,
                         bf16_stages(BM, GATED ? 2 * BNZ : BNZ), bf16_rb(BM)>;
 
+// Launches the tile for (block_m, bnz) and returns 0, or returns -1
+// without launching when no such tile exists; with p == nullptr it only
+// answers whether the tile exists.
+template <class C>
+static int run(const GemmParams* p, int64_t max_mblk, hipStream_t s) {
+  if (p) launch_gemm<C>(*p, max_mblk, s);
+  return 0;
+}
+
 template <int AM, int EP, bool GATED>
-static void dispatch_bm(int block_m, int bnz, const GemmParams& p, int64_t max_mblk,
-                        hipStream_t s) {
-  if (block_m == 16) {
-    if (bnz == 64) launch_gemm<Bf16Cfg<16, 64, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
-    else launch_gemm<Bf16Cfg<16, 128, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
-  } else if (block_m == 32) {
-    if (bnz == 64) launch_gemm<Bf16Cfg<32, 64, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
-    else launch_gemm<Bf16Cfg<32, 128, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
-  } else if (block_m == 64) {
-    if (bnz == 64) launch_gemm<Bf16Cfg<64, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
-    else launch_gemm<Bf16Cfg<64, 128, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
-  } else if (block_m == 128) {
-    if (bnz == 64) launch_gemm<Bf16Cfg<128, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
-    else launch_gemm<Bf16Cfg<128, 128, kW128M, kW128N, 32, GATED, AM, EP>>(p, max_mblk, s);
-  } else {
-    if (bnz == 64) launch_gemm<Bf16Cfg<256, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
-    else if (bnz == 128) launch_gemm<Bf16Cfg<256, 128, kW256M, kW256N, 32, GATED, AM, EP>>(p, max_mblk, s);
-    else launch_gemm<Bf16Cfg<256, 256, kW256M, kW256N, 32, false, AM, EP>>(p, max_mblk, s);
+static int dispatch_bm(int block_m, int bnz, const GemmParams* p, int64_t max_mblk,
+                       hipStream_t s) {
+  if (bnz != 64 && bnz != 128 && !(bnz == 256 && !GATED && block_m == 256)) return -1;
+  switch (block_m) {
+    case 16:
+      return bnz == 64 ? run<Bf16Cfg<16, 64, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s)
+                       : run<Bf16Cfg<16, 128, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
+    case 32:
+      return bnz == 64 ? run<Bf16Cfg<32, 64, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s)
+                       : run<Bf16Cfg<32, 128, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
+    case 64:
+      return bnz == 64 ? run<Bf16Cfg<64, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s)
+                       : run<Bf16Cfg<64, 128, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
+    case 128:
+      return bnz == 64 ? run<Bf16Cfg<128, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s)
+                       : run<Bf16Cfg<128, 128, kW128M, kW128N, 32, GATED, AM, EP>>(p, max_mblk, s);
+    case 256:
+      if (bnz == 64) return run<Bf16Cfg<256, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
+      if (bnz == 128) return run<Bf16Cfg<256, 128, kW256M, kW256N, 32, GATED, AM, EP>>(p, max_mblk, s);
+      if constexpr (!GATED) return run<Bf16Cfg<256, 256, kW256M, kW256N, 32, false, AM, EP>>(p, max_mblk, s);
+      return -1;
+    default:
+      return -1;
   }
 }
 
-void launch_gemm_bf16(int kind, bool gated, int block_m, int bnz, const GemmParams& p,
-                      int64_t max_mblk, hipStream_t s) {
+int launch_gemm_bf16(int kind, bool gated, int block_m, int bnz, const GemmParams* p,
+                     int64_t max_mblk, hipStream_t s) {
   switch (kind) {
     case GEMM_Z_ROUTED:
-      if (gated) dispatch_bm<A_GATHER, EPI_Z, true>(block_m, bnz, p, max_mblk, s);
-      else dispatch_bm<A_GATHER, EPI_Z, false>(block_m, bnz, p, max_mblk, s);
-      break;
+      return gated ? dispatch_bm<A_GATHER, EPI_Z, true>(block_m, bnz, p, max_mblk, s)
+                   : dispatch_bm<A_GATHER, EPI_Z, false>(block_m, bnz, p, max_mblk, s);
     case GEMM_Y_ROUTED:
-      dispatch_bm<A_ROWS, EPI_OUT_ROUTED, false>(block_m, bnz, p, max_mblk, s);
-      break;
+      return dispatch_bm<A_ROWS, EPI_OUT_ROUTED, false>(block_m, bnz, p, max_mblk, s);
     case GEMM_Z_DENSE:
-      if (gated) dispatch_bm<A_DENSE, EPI_Z, true>(block_m, bnz, p, max_mblk, s);
-      else dispatch_bm<A_DENSE, EPI_Z, false>(block_m, bnz, p, max_mblk, s);
-      break;
+      return gated ? dispatch_bm<A_DENSE, EPI_Z, true>(block_m, bnz, p, max_mblk, s)
+                   : dispatch_bm<A_DENSE, EPI_Z, false>(block_m, bnz, p, max_mblk, s);
+    case GEMM_Y_DENSE:
+      return dispatch_bm<A_DENSE, EPI_OUT_DENSE, false>(block_m, bnz, p, max_mblk, s);
     default:
-      dispatch_bm<A_DENSE, EPI_OUT_DENSE, false>(block_m, bnz, p, max_mblk, s);
-      break;
+      return -1;
   }
 }
 

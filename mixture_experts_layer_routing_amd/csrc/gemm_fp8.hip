@@ -11,48 +11,61 @@
 
 namespace moe {
 
+// Each dispatcher launches the tile for (block_m, width) and returns 0, or
+// returns -1 without launching when no such tile exists.  With p == nullptr
+// it only answers whether the tile exists (the host asks before it
+// enqueues anything).
+template <class C>
+static int run(const GemmParams* p, int64_t max_mblk, hipStream_t s) {
+  if (p) launch_gemm<C>(*p, max_mblk, s);
+  return 0;
+}
+
 template <int AM, int EP, bool GATED>
-static void dispatch_bm(int block_m, const GemmParams& p, int64_t max_mblk, hipStream_t s) {
+static int dispatch_bm(int block_m, const GemmParams* p, int64_t max_mblk, hipStream_t s) {
   switch (block_m) {
-    case 16: launch_gemm<GemmCfg<16, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s); break;
-    case 32: launch_gemm<GemmCfg<32, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s); break;
-    case 64: launch_gemm<GemmCfg<64, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s); break;
-    case 128: launch_gemm<GemmCfg<128, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s); break;
-    default:
+    case 16: return run<GemmCfg<16, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s);
+    case 32: return run<GemmCfg<32, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s);
+    case 64: return run<GemmCfg<64, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s);
+    case 128: return run<GemmCfg<128, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s);
+    case 256:
       // 256-row tiles exist for the ungated GEMMs only (a gated 256-row
-      // tile does not fit the registers); the host never asks for one
-      if constexpr (!GATED) launch_gemm<GemmCfg<256, 128, 2, 4, 32, true, false, AM, EP>>(p, max_mblk, s);
-      break;
+      // tile does not fit the registers)
+      if constexpr (!GATED) return run<GemmCfg<256, 128, 2, 4, 32, true, false, AM, EP>>(p, max_mblk, s);
+      return -1;
+    default:
+      return -1;
   }
 }
 
 // Second GEMMs of 16 or 32 rows on 256-column tiles (gemm_tile_n): each
 // wave's 64 columns stay inside one 128-row weight-scale block.
 template <int AM, int EP>
-static void dispatch_wide(int block_m, const GemmParams& p, int64_t max_mblk, hipStream_t s) {
-  if (block_m == 16) launch_gemm<GemmCfg<16, 256, 1, 4, 16, true, false, AM, EP>>(p, max_mblk, s);
-  else launch_gemm<GemmCfg<32, 256, 1, 4, 16, true, false, AM, EP>>(p, max_mblk, s);
+static int dispatch_wide(int block_m, const GemmParams* p, int64_t max_mblk, hipStream_t s) {
+  if (block_m == 16) return run<GemmCfg<16, 256, 1, 4, 16, true, false, AM, EP>>(p, max_mblk, s);
+  if (block_m == 32) return run<GemmCfg<32, 256, 1, 4, 16, true, false, AM, EP>>(p, max_mblk, s);
+  return -1;
 }
 
-void launch_gemm_fp8(int kind, bool gated, int block_m, int bnz, const GemmParams& p,
-                     int64_t max_mblk, hipStream_t s) {
+int launch_gemm_fp8(int kind, bool gated, int block_m, int bnz, const GemmParams* p,
+                    int64_t max_mblk, hipStream_t s) {
+  const bool first = kind == GEMM_Z_ROUTED || kind == GEMM_Z_DENSE;
+  if (bnz != 128 && !(bnz == 256 && !first)) return -1;
   switch (kind) {
     case GEMM_Z_ROUTED:
-      if (gated) dispatch_bm<A_GATHER, EPI_Z, true>(block_m, p, max_mblk, s);
-      else dispatch_bm<A_GATHER, EPI_Z, false>(block_m, p, max_mblk, s);
-      break;
+      return gated ? dispatch_bm<A_GATHER, EPI_Z, true>(block_m, p, max_mblk, s)
+                   : dispatch_bm<A_GATHER, EPI_Z, false>(block_m, p, max_mblk, s);
     case GEMM_Y_ROUTED:
-      if (bnz == 256) dispatch_wide<A_ROWS, EPI_OUT_ROUTED>(block_m, p, max_mblk, s);
-      else dispatch_bm<A_ROWS, EPI_OUT_ROUTED, false>(block_m, p, max_mblk, s);
-      break;
+      return bnz == 256 ? dispatch_wide<A_ROWS, EPI_OUT_ROUTED>(block_m, p, max_mblk, s)
+                        : dispatch_bm<A_ROWS, EPI_OUT_ROUTED, false>(block_m, p, max_mblk, s);
     case GEMM_Z_DENSE:
-      if (gated) dispatch_bm<A_DENSE, EPI_Z, true>(block_m, p, max_mblk, s);
-      else dispatch_bm<A_DENSE, EPI_Z, false>(block_m, p, max_mblk, s);
-      break;
+      return gated ? dispatch_bm<A_DENSE, EPI_Z, true>(block_m, p, max_mblk, s)
+                   : dispatch_bm<A_DENSE, EPI_Z, false>(block_m, p, max_mblk, s);
+    case GEMM_Y_DENSE:
+      return bnz == 256 ? dispatch_wide<A_DENSE, EPI_OUT_DENSE>(block_m, p, max_mblk, s)
+                        : dispatch_bm<A_DENSE, EPI_OUT_DENSE, false>(block_m, p, max_mblk, s);
     default:
-      if (bnz == 256) dispatch_wide<A_DENSE, EPI_OUT_DENSE>(block_m, p, max_mblk, s);
-      else dispatch_bm<A_DENSE, EPI_OUT_DENSE, false>(block_m, p, max_mblk, s);
-      break;
+      return -1;
   }
 }
 

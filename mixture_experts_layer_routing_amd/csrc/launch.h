@@ -88,10 +88,11 @@ enum GemmKind {
 // columns for the second) for an output of n columns.
 int gemm_tile_n(int kind, bool fp8, bool gated, int block_m, int n);
 // Launch one grouped GEMM with output tile bnz; max_mblk bounds the M-blocks
-// (grid sizing).
-void launch_gemm_bf16(int kind, bool gated, int block_m, int bnz, const GemmParams& p,
-                      int64_t max_mblk, hipStream_t s);
-void launch_gemm_fp8(int kind, bool gated, int block_m, int bnz, const GemmParams& p,
+// (grid sizing).  Returns 0, or -1 (nothing launched) when no tile of that
+// (kind, gated, block_m, bnz) exists.  p == nullptr only asks the question.
+int launch_gemm_bf16(int kind, bool gated, int block_m, int bnz, const GemmParams* p,
                      int64_t max_mblk, hipStream_t s);
+int launch_gemm_fp8(int kind, bool gated, int block_m, int bnz, const GemmParams* p,
+                    int64_t max_mblk, hipStream_t s);
 
 }  // namespace moe

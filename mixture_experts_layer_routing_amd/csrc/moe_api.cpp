@@ -52,6 +52,23 @@ bool quant_fp8(int quant) {
   return quant == MOE_QUANT_FP8_G128 || quant == MOE_QUANT_FP8_TOKEN ||
          quant == MOE_QUANT_FP8_TENSOR;
 }
+// The prepare quant_config: a known format with the one group and weight
+// block size the kernels implement (128; the per-token and per-tensor
+// formats have no channel group).
+int check_quant_config(const moe_quant_config* qc) {
+  if (!qc) return fail(MOE_ERR_INVALID_ARG, "quant_config is NULL");
+  if (qc->quant == MOE_QUANT_NONE) return MOE_OK;
+  if (!quant_fp8(qc->quant)) return fail(MOE_ERR_UNSUPPORTED, "quant %d not supported", qc->quant);
+  const int group = qc->quant == MOE_QUANT_FP8_G128 ? 128 : 0;
+  if (qc->act_group != group)
+    return fail(MOE_ERR_UNSUPPORTED, "act_group %d: quant %d takes %d", qc->act_group, qc->quant,
+                group);
+  if (qc->w_block_n != 128 || qc->w_block_k != 128)
+    return fail(MOE_ERR_UNSUPPORTED, "weight blocks %dx%d: only 128x128", qc->w_block_n,
+                qc->w_block_k);
+  return MOE_OK;
+}
+
 // fp32 scales of an fp8 [rows, K] activation in the given format
 size_t act_scale_count(int quant, int64_t rows, int K) {
   if (quant == MOE_QUANT_FP8_G128) return static_cast<size_t>(rows) * (K / 128);
@@ -280,6 +297,36 @@ struct StageEvents {
   }
 };
 
+// Whether a GEMM tile exists for each of the four launches the experts
+// stage would make (routed first and second GEMM, shared expert's two):
+// asked before anything is enqueued, so an unsupported request leaves no
+// partial work behind.
+int tiles_exist(int T, int H, const moe_weights* w, int activation, int bm) {
+  using namespace moe;
+  const bool fp8 = quant_fp8(w->quant);
+  const bool gated = act_gated(activation);
+  auto has = [&](int kind, int blk_m, int bnz) {
+    return (fp8 ? launch_gemm_fp8(kind, gated, blk_m, bnz, nullptr, 0, nullptr)
+                : launch_gemm_bf16(kind, gated, blk_m, bnz, nullptr, 0, nullptr)) == 0;
+  };
+  const int bm1 = first_gemm_bm(fp8, gated, bm);
+  const int bm2 = second_gemm_bm(fp8, bm);
+  struct Q { int kind, bm, bn; } q[4] = {
+      {GEMM_Z_ROUTED, bm1, gemm_tile_n(GEMM_Z_ROUTED, fp8, gated, bm1, w->inter)},
+      {GEMM_Y_ROUTED, bm2, gemm_tile_n(GEMM_Y_ROUTED, fp8, gated, bm2, H)}, {0, 0, 0}, {0, 0, 0}};
+  int nq = 2;
+  if (w->shared_inter > 0) {
+    const int dbm3 = dense_block_m(T, fp8, true), dbm4 = dense_block_m(T, fp8, false);
+    q[nq++] = {GEMM_Z_DENSE, dbm3, gemm_tile_n(GEMM_Z_DENSE, fp8, gated, dbm3, w->shared_inter)};
+    q[nq++] = {GEMM_Y_DENSE, dbm4, gemm_tile_n(GEMM_Y_DENSE, fp8, gated, dbm4, H)};
+  }
+  for (int i = 0; i < nq; ++i)
+    if (!has(q[i].kind, q[i].bm, q[i].bn))
+      return fail(MOE_ERR_UNSUPPORTED, "no %s GEMM tile for kind %d, %d rows x %d columns%s",
+                  fp8 ? "fp8" : "bf16", q[i].kind, q[i].bm, q[i].bn, gated ? " (gated)" : "");
+  return MOE_OK;
+}
+
 int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
                 const float* shared_in_scale, const Routed& rt, int T, int H, const moe_weights* w,
                 int activation, const int32_t* sorted, const int32_t* block_expert,
@@ -299,9 +346,10 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   const Caps& cp = rt.cp;
   const int64_t rows = cp.block_cap * bm;
   const int nflat = rt.T * rt.top_k;
+  // every tile was checked to exist before anything was enqueued (tiles_exist)
   auto launch = [&](int kind, int blk_m, int bnz, const GemmParams& p, int64_t max_mblk) {
-    if (fp8) launch_gemm_fp8(kind, gated, blk_m, bnz, p, max_mblk, s);
-    else launch_gemm_bf16(kind, gated, blk_m, bnz, p, max_mblk, s);
+    if (fp8) (void)launch_gemm_fp8(kind, gated, blk_m, bnz, &p, max_mblk, s);
+    else (void)launch_gemm_bf16(kind, gated, blk_m, bnz, &p, max_mblk, s);
   };
   const int act = act_fn(activation);
   auto split = [&](GemmParams& g, int S, int64_t part_rows, int ldp) {
@@ -464,17 +512,19 @@ int moe_route(const float* logits, int T, int E, int top_k, int scoring, int ren
   return check_launch("moe_route");
 }
 
-int moe_prepare(const uint16_t* a1, int T, int H, const float* topk_weights, int top_k,
-                int apply_router_weight_on_input, int quant, void* a1q, float* a1q_scale,
-                hipStream_t stream) {
+int moe_prepare(const uint16_t* a1, int T, int H, const float* topk_weights,
+                const int32_t* topk_ids, int top_k, int apply_router_weight_on_input,
+                const moe_quant_config* qc, void* a1q, float* a1q_scale, hipStream_t stream) {
   g_err[0] = 0;
+  (void)topk_ids;   // no dispatch without expert parallelism: the ids pass through
+  if (int st = check_quant_config(qc)) return st;
+  const int quant = qc->quant;
   if (T < 0 || H <= 0 || H % 8) return fail(MOE_ERR_INVALID_ARG, "T=%d H=%d", T, H);
-  if (quant != MOE_QUANT_NONE && !quant_fp8(quant))
-    return fail(MOE_ERR_UNSUPPORTED, "quant %d not supported", quant);
   if (quant_fp8(quant) && H % 128)
     return fail(MOE_ERR_INVALID_ARG, "fp8 needs H %% 128 == 0 (H=%d)", H);
   if (quant == MOE_QUANT_FP8_TOKEN && H > 16384)
     return fail(MOE_ERR_UNSUPPORTED, "per-token fp8 holds a row in registers: H=%d > 16384", H);
+  if (top_k < 1) return fail(MOE_ERR_INVALID_ARG, "top_k=%d < 1", top_k);
   if (apply_router_weight_on_input && top_k != 1)
     return fail(MOE_ERR_INVALID_ARG, "router weight on the input needs top_k == 1 (got %d)", top_k);
   if (T == 0) return MOE_OK;
@@ -574,6 +624,7 @@ int moe_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   const size_t need = moe_experts_workspace_bytes(T, H, top_k, weights, activation, block_m);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "experts workspace %zu < %zu", workspace_bytes, need);
+  if (int st = tiles_exist(T, H, weights, activation, block_m)) return st;
   return run_experts(a1q, a1q_scale, shared_in, shared_in_scale,
                      standard_rows(T, top_k, weights->num_experts, block_m), T, H, weights,
                      activation, sorted_token_ids, block_expert_ids, num_tokens_post_padded, block_m,
@@ -674,6 +725,7 @@ int moe_experts_batched(const void* a, const float* a_scale, const int32_t* expe
   const size_t need = batched_layout(max_tokens, H, &w, activation, bm, nullptr, &L);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "batched experts workspace %zu < %zu", workspace_bytes, need);
+  if (int st = tiles_exist(0, H, &w, activation, bm)) return st;
   batched_layout(max_tokens, H, &w, activation, bm, workspace, &L);
   const Routed rt = batched_rows(E, max_tokens, bm);
   moe::launch_batched_schedule(expert_num_tokens, E, max_tokens, bm, rt.cp.block_cap, L.sorted,
@@ -805,6 +857,7 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
                                      apply_router_weight_on_input, nullptr, &L);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "forward workspace %zu < %zu", workspace_bytes, need);
+  if (int st = tiles_exist(T, H, weights, activation, bm)) return st;
   forward_layout(T, H, top_k, weights, activation, bm, apply_router_weight_on_input, workspace,
                  &L);
   const StageEvents se{stage_events, stream};

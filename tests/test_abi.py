@@ -90,12 +90,51 @@ def test_validation_happens_before_any_launch(moe):
     assert L.moe_route(null, 4, 8, 2, 7, 1, null, null, null) == 1
     # T == 0 is a no-op and touches no pointer
     assert L.moe_route(null, 0, 8, 2, 0, 1, null, null, null) == 0
-    # weight on the input needs top_k == 1 (the pages' assert)
-    assert L.moe_prepare(null, 4, 128, null, 2, 1, 0, null, null, null) == 1
+    # prepare(a1, topk_weights, topk_ids, ..., apply_router_weight_on_input,
+    # quant_config): weight on the input needs top_k == 1 (the pages' assert)
+    qc = moe.binding.quant_config
+    none, g128 = ctypes.byref(qc("none")), ctypes.byref(qc("fp8"))
+    assert L.moe_prepare(null, 4, 128, null, null, 2, 1, none, null, null, null) == 1
     assert "top_k == 1" in moe.last_error()
-    # fp8 needs H % 128 == 0; unknown quant is unsupported
-    assert L.moe_prepare(null, 4, 136, null, 1, 0, 1, null, null, null) == 1
-    assert L.moe_prepare(null, 4, 128, null, 1, 0, 5, null, null, null) == 2
+    # fp8 needs H % 128 == 0; an unknown quant is unsupported; no config at all
+    assert L.moe_prepare(null, 4, 136, null, null, 1, 0, g128, null, null, null) == 1
+    bad = moe.binding.MoeQuantConfig(5, 128, 128, 128)
+    assert L.moe_prepare(null, 4, 128, null, null, 1, 0, ctypes.byref(bad), null, null, null) == 2
+    assert L.moe_prepare(null, 4, 128, null, null, 1, 0, null, null, null, null) == 1
+    assert "quant_config" in moe.last_error()
+
+
+@pytest.mark.parametrize("cfg", [("fp8", 64, 128, 128), ("fp8", 128, 128, 64),
+                                 ("fp8", 128, 256, 128), ("fp8_token", 128, 128, 128),
+                                 ("fp8_tensor", 7, 128, 128)])
+def test_prepare_rejects_unsupported_group_and_block_sizes(moe, cfg):
+    """Only the G(128) group (none for per-token/per-tensor scales) and
+    128x128 weight blocks are implemented; anything else is unsupported,
+    reported before any launch (the pointers here are all NULL)."""
+    quant, group, bn, bk = cfg
+    qc = moe.binding.MoeQuantConfig(moe.binding.QUANT[quant], group, bn, bk)
+    assert moe.binding.lib().moe_prepare(None, 4, 256, None, None, 1, 0, ctypes.byref(qc), None,
+                                         None, None) == 2
+
+
+def test_prepare_accepts_the_implemented_configs_and_ignores_topk_ids(moe):
+    """The implemented configs pass validation (T == 0: a no-op that reads
+    no pointer); topk_ids may be NULL or anything, it is not read."""
+    L = moe.binding.lib()
+    for quant in ("none", "fp8", "fp8_token", "fp8_tensor"):
+        qc = moe.binding.quant_config(quant)
+        assert L.moe_prepare(None, 0, 256, None, None, 1, 0, ctypes.byref(qc), None, None,
+                             None) == 0
+        assert L.moe_prepare(None, 0, 256, None, 12345, 1, 0, ctypes.byref(qc), None, None,
+                             None) == 0
+    # quant NONE ignores the group and block fields
+    qc = moe.binding.MoeQuantConfig(0, 7, 3, 5)
+    assert L.moe_prepare(None, 0, 256, None, None, 1, 0, ctypes.byref(qc), None, None, None) == 0
+
+
+def test_validation_happens_before_any_launch_continued(moe):
+    L = moe.binding.lib()
+    null = None
     # align: bad block size, E too large
     assert L.moe_align(null, 4, 2, 8, 48, null, null, null, null, null, null, 0, null) == 1
     assert L.moe_align(null, 4, 2, 2000, 16, null, null, null, null, null, null, 0, null) == 1

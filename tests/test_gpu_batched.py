@@ -45,7 +45,7 @@ def _quantise(moe, spec, a):
     host = to_numpy_bits(a)
     if spec.quant == "none":
         return a, None, host, None
-    q, s = moe.moe_prepare(a.reshape(E * M, H), None, False, spec.quant)
+    q, s = moe.moe_prepare(a.reshape(E * M, H), quant=spec.quant)
     rq, rs = oracle.prepare(host.reshape(E * M, H), None, False, spec.quant)
     np.testing.assert_array_equal(to_numpy_bits(q), rq)
     np.testing.assert_array_equal(s.cpu().numpy().reshape(rs.shape), rs)
@@ -188,7 +188,7 @@ def test_batched_matches_standard_rows(spec, bm):
     moe = _moe()
     d = {k: v.to(DEV) for k, v in make_layer_inputs(spec).items()}
     ids, tw = moe.moe_route(d["logits"], spec.top_k, spec.scoring, spec.renormalize)
-    a1q, a1s = moe.moe_prepare(d["x"], tw, False, spec.quant)
+    a1q, a1s = moe.moe_prepare(d["x"], tw, quant=spec.quant)
     w = _weights(moe, d, spec.quant)
     al = moe.moe_align(ids, spec.E, bm)
     feo, _ = moe.moe_experts(a1q, a1s, w, spec.top_k, al, bm, spec.activation)

@@ -91,7 +91,7 @@ def test_experts_outputs_ignore_padding_and_workspace_contents(name, BM):
     rid, rw = oracle.route(d["logits"].numpy(), spec.top_k, spec.scoring, spec.renormalize)
     ids = torch.from_numpy(rid).to(DEV)
     tw = torch.from_numpy(rw).to(DEV)
-    a1q, a1s = moe.moe_prepare(dd["x"], tw, spec.apply_router_weight_on_input, spec.quant)
+    a1q, a1s = moe.moe_prepare(dd["x"], tw, ids, spec.apply_router_weight_on_input, spec.quant)
     al = moe.moe_align(ids, spec.E, BM)
     w = _weights(moe, dd, spec.quant)
     nbytes = moe.binding.lib().moe_experts_workspace_bytes(
@@ -119,12 +119,12 @@ def _experts_case(spec, BM):
     ra, rs = oracle.prepare(x_bits, rw, spec.apply_router_weight_on_input, spec.quant)
     ids = torch.from_numpy(rid).to(DEV)
     tw = torch.from_numpy(rw).to(DEV)
-    a1q, a1s = moe.moe_prepare(dd["x"], tw, spec.apply_router_weight_on_input, spec.quant)
+    a1q, a1s = moe.moe_prepare(dd["x"], tw, ids, spec.apply_router_weight_on_input, spec.quant)
     sh_in, sh_s = None, None
     shared = None
     if spec.shared_I:
         if spec.apply_router_weight_on_input:
-            sh_in, sh_s = moe.moe_prepare(dd["x"], None, False, spec.quant)
+            sh_in, sh_s = moe.moe_prepare(dd["x"], quant=spec.quant)
             sa, ss = oracle.prepare(x_bits, None, False, spec.quant)
         else:
             sa, ss = ra, rs

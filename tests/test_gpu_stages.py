@@ -90,7 +90,8 @@ def test_prepare_bit_exact(T, H, flag, quant):
     x = (torch.randn((T, H), generator=g) * torch.rand((T, 1), generator=g) * 10).to(torch.bfloat16)
     x[0, :8] = 0.0                                   # a zero run (zero group when H == 8)
     tw = torch.rand((T, 1), generator=g) if flag else None
-    q, s = moe.moe_prepare(x.to(DEV), None if tw is None else tw.to(DEV), flag, quant)
+    q, s = moe.moe_prepare(x.to(DEV), None if tw is None else tw.to(DEV),
+                           apply_router_weight_on_input=flag, quant=quant)
     torch.cuda.synchronize()
     rq, rs = oracle.prepare(to_numpy_bits(x), None if tw is None else tw.numpy(), flag, quant)
     np.testing.assert_array_equal(to_numpy_bits(q), rq)
@@ -103,7 +104,7 @@ def test_prepare_zero_group_and_constant_group():
     x = torch.zeros((2, 256), dtype=torch.bfloat16)
     x[1, :128] = -3.0
     x[1, 128:] = 448.0
-    q, s = moe.moe_prepare(x.to(DEV), None, False, "fp8")
+    q, s = moe.moe_prepare(x.to(DEV), quant="fp8")
     torch.cuda.synchronize()
     rq, rs = oracle.prepare(to_numpy_bits(x), None, False, "fp8")
     np.testing.assert_array_equal(to_numpy_bits(q), rq)
@@ -114,7 +115,7 @@ def test_prepare_rejects_weight_on_input_with_top_k_2():
     moe = _moe()
     x = torch.zeros((4, 128), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(moe.MoeError):
-        moe.moe_prepare(x, torch.ones((4, 2), device=DEV), True, "none")
+        moe.moe_prepare(x, torch.ones((4, 2), device=DEV), apply_router_weight_on_input=True)
 
 
 # ------------------------------------------------------------------ align
