@@ -50,10 +50,10 @@ def f64_to_bf16_bits(x):
     return np.where(np.isnan(x), np.uint16(0x7FC0), out).astype(np.uint16)
 
 
-def e4m3_decode(codes):
-    """OCP E4M3 codes (uint8) -> float64 by the format's closed form:
-    sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0;
-    exponent field 0 is subnormal (mantissa * 2**-9); 0x7F/0xFF are NaN."""
+def _e4m3_closed_form(codes):
+    """OCP E4M3 codes -> float64 by the format's closed form: sign bit 7,
+    exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent field 0 is
+    subnormal (mantissa * 2**-9); 0x7F/0xFF are NaN."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
@@ -62,6 +62,15 @@ def e4m3_decode(codes):
                    (1.0 + m / 8.0) * np.ldexp(1.0, (e - 7).astype(np.int64)))
     val = sign * mag
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+# The closed form evaluated once on all 256 codes; decoding is a lookup.
+_E4M3_VALUES = _e4m3_closed_form(np.arange(256, dtype=np.uint8))
+
+
+def e4m3_decode(codes):
+    """OCP E4M3 codes (uint8) -> float64: the closed form above, looked up."""
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_encode_sat(x):

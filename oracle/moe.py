@@ -259,7 +259,13 @@ def dequant_weight(w, scale):
         return bf16_bits_to_f64(w)
     v = e4m3_decode(w)
     s = np.asarray(scale, dtype=np.float64)
-    return v * np.repeat(np.repeat(s, WBLOCK, axis=0), WBLOCK, axis=1)[:v.shape[0], :v.shape[1]]
+    N, K = v.shape
+    if N % WBLOCK == 0 and K % WBLOCK == 0:
+        # each 128x128 block times its scale (a view of v by blocks)
+        blocks = v.reshape(N // WBLOCK, WBLOCK, K // WBLOCK, WBLOCK)
+        blocks *= s[:N // WBLOCK, None, :K // WBLOCK, None]
+        return v
+    return v * np.repeat(np.repeat(s, WBLOCK, axis=0), WBLOCK, axis=1)[:N, :K]
 
 
 def _scale_rows(scale, tok):
