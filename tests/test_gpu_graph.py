@@ -6,7 +6,8 @@ bit for bit (the kernels are deterministic: align has no order-dependent
 atomics, split-K partials are summed in split order).  Each case replays
 the graph several times with new inputs written in place, with eager work
 and host synchronisations between the replays, and checks every replay.
-The eager path itself is checked against the oracle elsewhere."""
+The last replay is also checked against the oracle, to the same bar as
+the eager forward."""
 
 import sys
 
@@ -14,7 +15,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from workloads import PARITY_CASES, make_layer_inputs, to_numpy_bits
+from helpers import check_tolerance, f64_of_bf16, f64_of_fp8, output_allowance
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -83,6 +86,7 @@ def test_graph_replays_match_eager(spec):
                 again, _ = g.launch(s)
             s.synchronize()
             np.testing.assert_array_equal(to_numpy_bits(again), to_numpy_bits(want))
+        _check_against_oracle(spec, d, xi, li, out.clone(), None if out_s is None else out_s.clone())
     finally:
         g.close()
 
@@ -95,3 +99,25 @@ def test_graph_on_default_stream_is_rejected():
     with pytest.raises(ValueError):
         with torch.cuda.stream(torch.cuda.default_stream()):
             moe.ForwardGraph(d["x"], d["logits"], w, spec.top_k)
+
+
+def _check_against_oracle(spec, d, x, logits, out, out_s):
+    hw = {k: to_numpy_bits(d[k]) for k in d if k.startswith(("w13", "w2", "shared"))}
+    gamma = to_numpy_bits(d.get("gamma"))
+    refs = {mode: oracle.forward(to_numpy_bits(x), logits.cpu().numpy(), hw, spec.top_k,
+                                 spec.scoring, spec.renormalize, 16,
+                                 spec.apply_router_weight_on_input, spec.quant, spec.activation,
+                                 mode, to_numpy_bits(d.get("residual")), gamma, spec.eps,
+                                 spec.out_quant)
+            for mode in ("exact", "mirrored")}
+    if spec.out_quant == "fp8":
+        got = f64_of_fp8(out, out_s)
+        ref = {m: f64_of_fp8(r["output"], r["output_scale"]) for m, r in refs.items()}
+    else:
+        got = f64_of_bf16(out)
+        ref = {m: f64_of_bf16(r["output"]) for m, r in refs.items()}
+    fp8 = spec.quant.startswith("fp8") or spec.out_quant == "fp8"
+    d_now = dict(d, x=x)
+    allowance, slack = output_allowance(spec, refs["mirrored"], d_now, hw)
+    check_tolerance(got, ref["exact"], ref["mirrored"], "fp8" if fp8 else "bf16",
+                    f"graph {spec.name} vs oracle", allowance=allowance, maxnorm_slack=slack)

@@ -34,7 +34,8 @@ def _refinalize(spec, d, ref, feo, tw=None):
 def _check(spec, d, ref, got):
     exact = f64_of_bf16(ref["output"])
     return check_tolerance(got, exact, exact, "bf16", spec.name,
-                           allowance=finalize_flip_allowance(ref, to_numpy_bits(d.get("gamma"))))
+                           allowance=finalize_flip_allowance(ref, to_numpy_bits(d.get("gamma")),
+                                                             spec.apply_router_weight_on_input))
 
 
 @pytest.mark.parametrize("spec", CASES, ids=lambda s: s.name)
@@ -67,3 +68,19 @@ def test_planted_mistakes_fail(spec):
     swapped[0], swapped[-1] = feo[-1], feo[0]      # rows of two tokens exchanged
     with pytest.raises(AssertionError):
         _check(spec, d, ref, _refinalize(spec, d, ref, swapped))
+
+
+def test_flip_allowance_uses_weight_one_when_the_weight_went_on_the_input():
+    """With the router weight on the input, finalize adds the expert row
+    with weight 1, so a one-step flip of that row moves the output by a
+    whole step of the row, not by w times it."""
+    spec = next(s for s in CASES if s.apply_router_weight_on_input)
+    d, ref = _forward(spec)
+    tok = ref["tokens"]
+    y = f64_of_bf16(ref["fused_expert_output"])[tok][:, 0]
+    from helpers import bf16_ulp
+    allow = finalize_flip_allowance(ref, None, weight_on_input=True)
+    assert np.all(allow >= bf16_ulp(y))
+    w = np.asarray(ref["topk_weights"], np.float64)[tok]
+    assert w.max() < 1.0          # the weighted allowance would be smaller
+    assert np.any(finalize_flip_allowance(ref, None) < bf16_ulp(y))
