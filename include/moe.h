@@ -378,6 +378,29 @@ int moe_forward_graph_launch(moe_graph* graph, hipStream_t stream);
 /* Releases the graph (NULL is a no-op); no replay of it may still be pending. */
 int moe_forward_graph_destroy(moe_graph* graph);
 
+/*
+ * moe_forward_noalloc -- moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same layer, arguments and results as moe_forward,
+ * with its workspace taken from a scratch array of MOE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) compiled into the library, one per GPU, held from the first call
+ * on that GPU until the process ends.  The call allocates nothing.  Sizes
+ * whose moe_forward_workspace_bytes exceeds the scratch (beyond decode
+ * sizes: e.g. T = 128 fits every layer shape of the workloads here) return
+ * MOE_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares that GPU's scratch, so calls that overlap on one GPU (two streams,
+ * or two host threads) race and must be serialised by the caller; calls in
+ * one stream's order are fine.  The first call on a GPU looks up the
+ * scratch's address there (MOE_ERR_HIP if that fails).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const uint16_t* x, const float* logits, int T, int H, int top_k,
+                        int scoring, int renormalize, int apply_router_weight_on_input,
+                        const moe_weights* weights /* host */, int activation, int block_m,
+                        const uint16_t* residual, const uint16_t* gamma, float eps, int out_quant,
+                        void* output, float* output_scale, uint16_t* residual_out,
+                        hipStream_t stream);
+
 /* (host) the block_m moe_forward uses when given 0, by the average rows per
  * expert a = T*top_k/E: 16 (a <= 16), 32 (a <= 32), then bf16: 64 (a <= 64)
  * else 256; fp8: 64 (a <= 96), 128 (a <= 192) else 256.  quant is a moe_quant. */

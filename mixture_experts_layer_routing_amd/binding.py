@@ -102,6 +102,9 @@ def _load():
                                 c_vp, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp]),
         "moe_forward_workspace_bytes": (c_sz, [c_int, c_int, c_int, ctypes.POINTER(MoeWeights),
                                                c_int, c_int, c_int]),
+        "moe_forward_noalloc": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                        ctypes.POINTER(MoeWeights), c_int, c_int, c_vp, c_vp, c_f32,
+                                        c_int, c_vp, c_vp, c_vp, c_vp]),
         "moe_forward_graph_create": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                              ctypes.POINTER(MoeWeights), c_int, c_int, c_vp, c_vp,
                                              c_f32, c_int, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp,
@@ -373,6 +376,31 @@ def moe_forward(x, logits, weights, top_k, scoring="softmax", renormalize=True,
                             _ptr(residual_out), _ptr(workspace), wsb, ev, _stream(stream)),
            "moe_forward")
     return output, (output_scale if out_quant == "fp8" else None), workspace
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(x, logits, weights, top_k, scoring="softmax", renormalize=True,
+                        apply_router_weight_on_input=False, activation="silu", block_m=0,
+                        residual=None, gamma=None, eps=1e-6, out_quant="none", output=None,
+                        output_scale=None, residual_out=None, stream=None):
+    """moe_forward on the library's fixed per-GPU scratch: the library
+    allocates nothing (outputs not passed in are allocated here by torch)."""
+    T, H = x.shape
+    dev = x.device
+    if output is None:
+        output = torch.empty((T, H), dtype=torch.uint8 if out_quant == "fp8" else torch.bfloat16,
+                             device=dev)
+    if out_quant == "fp8" and output_scale is None:
+        output_scale = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+    _check(_lib.moe_forward_noalloc(_ptr(x), _ptr(logits), T, H, top_k, SCORING[scoring],
+                                    int(renormalize), int(apply_router_weight_on_input),
+                                    ctypes.byref(weights), ACTIVATION[activation], block_m,
+                                    _ptr(residual), _ptr(gamma), float(eps), QUANT[out_quant],
+                                    _ptr(output), _ptr(output_scale), _ptr(residual_out),
+                                    _stream(stream)), "moe_forward_noalloc")
+    return output, (output_scale if out_quant == "fp8" else None)
 
 
 class ForwardGraph:

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "launch.h"
@@ -826,13 +827,12 @@ size_t moe_forward_workspace_bytes(int T, int H, int top_k, const moe_weights* w
                         &L);
 }
 
-int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k, int scoring,
-                int renormalize, int apply_router_weight_on_input, const moe_weights* weights,
-                int activation, int block_m, const uint16_t* residual, const uint16_t* gamma,
-                float eps, int out_quant, void* output, float* output_scale,
-                uint16_t* residual_out, void* workspace, size_t workspace_bytes,
-                hipEvent_t* stage_events, hipStream_t stream) {
-  g_err[0] = 0;
+// The forward's argument checks (host only, nothing enqueued); *bm gets
+// the block size the call uses.  MOE_OK with T == 0 means a no-op.
+static int forward_args(const uint16_t* x, const float* logits, int T, int H, int top_k,
+                        int scoring, int apply_router_weight_on_input,
+                        const moe_weights* weights, int activation, int block_m, float eps,
+                        int out_quant, const void* output, const float* output_scale, int* bm) {
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
   if (int st = check_weights(weights, H, activation, true)) return st;
   const int E = weights->num_experts;
@@ -846,12 +846,29 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
   if (H > 16384) return fail(MOE_ERR_INVALID_ARG, "H=%d > 16384", H);
   if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
   if (static_cast<int64_t>(T) * top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
-  const int bm = block_m ? block_m : moe_pick_block_m(T, top_k, E, weights->quant);
-  if (!valid_block_m(bm)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", bm);
-  const bool fp8 = quant_fp8(weights->quant);
+  *bm = block_m ? block_m : moe_pick_block_m(T, top_k, E, weights->quant);
+  if (!valid_block_m(*bm)) return fail(MOE_ERR_INVALID_ARG, "block_m=%d", *bm);
   if (T == 0) return MOE_OK;
   if (!x || !logits || !output || (out_quant == MOE_QUANT_FP8_G128 && !output_scale))
     return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  return MOE_OK;
+}
+
+int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k, int scoring,
+                int renormalize, int apply_router_weight_on_input, const moe_weights* weights,
+                int activation, int block_m, const uint16_t* residual, const uint16_t* gamma,
+                float eps, int out_quant, void* output, float* output_scale,
+                uint16_t* residual_out, void* workspace, size_t workspace_bytes,
+                hipEvent_t* stage_events, hipStream_t stream) {
+  g_err[0] = 0;
+  int bm = 0;
+  if (int st = forward_args(x, logits, T, H, top_k, scoring, apply_router_weight_on_input,
+                            weights, activation, block_m, eps, out_quant, output, output_scale,
+                            &bm))
+    return st;
+  if (T == 0) return MOE_OK;
+  const int E = weights->num_experts;
+  const bool fp8 = quant_fp8(weights->quant);
   ForwardLayout L;
   const size_t need = forward_layout(T, H, top_k, weights, activation, bm,
                                      apply_router_weight_on_input, nullptr, &L);
@@ -964,6 +981,86 @@ int moe_forward_graph_destroy(moe_graph* graph) {
   if (a != hipSuccess || b != hipSuccess)
     return fail(MOE_ERR_HIP, "graph destroy: %s", hipGetErrorString(a != hipSuccess ? a : b));
   return MOE_OK;
+}
+
+}  // extern "C"
+
+// ---- moe_forward_noalloc: the forward on a fixed scratch array ----
+//
+// One array per GPU, defined here, held by each GPU the library runs on
+// until the process ends.  Host code never passes `scratch` itself (its
+// host-side name is a stand-in, not a device address): the device address
+// comes from hipGetSymbolAddress, once per device, and is kept per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that owns `stream` (the
+// current device for the null stream).
+int scratch_for(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    if (back != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipSetDevice(%d): %s", cur, hipGetErrorString(back));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_noalloc(const uint16_t* x, const float* logits, int T, int H, int top_k,
+                        int scoring, int renormalize, int apply_router_weight_on_input,
+                        const moe_weights* weights, int activation, int block_m,
+                        const uint16_t* residual, const uint16_t* gamma, float eps, int out_quant,
+                        void* output, float* output_scale, uint16_t* residual_out,
+                        hipStream_t stream) {
+  g_err[0] = 0;
+  int bm = 0;
+  if (int st = forward_args(x, logits, T, H, top_k, scoring, apply_router_weight_on_input,
+                            weights, activation, block_m, eps, out_quant, output, output_scale,
+                            &bm))
+    return st;
+  if (T == 0) return MOE_OK;
+  const size_t need = moe_forward_workspace_bytes(T, H, top_k, weights, activation, bm,
+                                                  apply_router_weight_on_input);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: these sizes need %zu bytes of scratch, above the fixed "
+                "%zu (use moe_forward with a workspace)",
+                need, static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (int st = scratch_for(stream, &ws)) return st;
+  // Every piece of the forward's workspace is written before it is read
+  // (align and the per-tensor scale clear their own counters with kernels),
+  // so stale contents from an earlier call do not matter.
+  return moe_forward(x, logits, T, H, top_k, scoring, renormalize, apply_router_weight_on_input,
+                     weights, activation, block_m, residual, gamma, eps, out_quant, output,
+                     output_scale, residual_out, ws, MOE_NOALLOC_SCRATCH_BYTES, nullptr, stream);
 }
 
 }  // extern "C"
