@@ -30,6 +30,15 @@ constexpr int kW128M = 2, kW128N = 4;
 template <int BM, int BNZ, int WM, int WN, int MF, bool GATED, int AM, int EP>
 using Bf16Cfg = GemmCfg<BM, BNZ, WM, WN, MF, false, GATED, AM, EP,
                         bf16_stages(BM, GATED ? 2 * BNZ : BNZ), bf16_rb(BM)>;
+// 256 x 256 tiles with split rings (GemmCfg::SPLIT): 2 A + 3 B k-tiles of
+// 32 KB, the whole 160 KB of LDS.  Measured on MI355X against the two-stage
+// tile: routed GEMMs at Llama-4 T=2048 and Mixtral T=512 (one 256-row block
+// or less per expert, weights streamed) 9-10 % faster; Mixtral T=4096 (four
+// blocks per expert) 2 % slower; the dense shared-expert GEMMs of Llama-4
+// T=2048 3-8 % slower, so launches choose (GemmParams::split_ring).
+constexpr bool kBf16Split = true;
+template <int BM, int BNZ, int WM, int WN, int MF, bool GATED, int AM, int EP>
+using Bf16Split = GemmCfg<BM, BNZ, WM, WN, MF, false, GATED, AM, EP, 2, 128, kBf16Split>;
 
 // Launches the tile for (block_m, bnz) and returns 0, or returns -1
 // without launching when no such tile exists; with p == nullptr it only
@@ -59,8 +68,16 @@ static int dispatch_bm(int block_m, int bnz, const GemmParams* p, int64_t max_mb
                        : run<Bf16Cfg<128, 128, kW128M, kW128N, 32, GATED, AM, EP>>(p, max_mblk, s);
     case 256:
       if (bnz == 64) return run<Bf16Cfg<256, 64, 2, 2, 32, GATED, AM, EP>>(p, max_mblk, s);
-      if (bnz == 128) return run<Bf16Cfg<256, 128, kW256M, kW256N, 32, GATED, AM, EP>>(p, max_mblk, s);
-      if constexpr (!GATED) return run<Bf16Cfg<256, 256, kW256M, kW256N, 32, false, AM, EP>>(p, max_mblk, s);
+      if (bnz == 128) {
+        if (p && p->split_ring)
+          return run<Bf16Split<256, 128, kW256M, kW256N, 32, GATED, AM, EP>>(p, max_mblk, s);
+        return run<Bf16Cfg<256, 128, kW256M, kW256N, 32, GATED, AM, EP>>(p, max_mblk, s);
+      }
+      if constexpr (!GATED) {
+        if (p && p->split_ring)
+          return run<Bf16Split<256, 256, kW256M, kW256N, 32, false, AM, EP>>(p, max_mblk, s);
+        return run<Bf16Cfg<256, 256, kW256M, kW256N, 32, false, AM, EP>>(p, max_mblk, s);
+      }
       return -1;
     default:
       return -1;

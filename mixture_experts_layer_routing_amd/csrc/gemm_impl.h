@@ -50,7 +50,7 @@ enum { A_GATHER = 0, A_ROWS = 1, A_DENSE = 2 };
 enum { EPI_Z = 0, EPI_OUT_ROUTED = 1, EPI_OUT_DENSE = 2 };
 
 template <int BM_, int BNZ_, int WAVES_M_, int WAVES_N_, int MF_, bool FP8_, bool GATED_,
-          int AMODE_, int EPI_, int NSTAGE_ = 2, int RB_ = 128>
+          int AMODE_, int EPI_, int NSTAGE_ = 2, int RB_ = 128, bool SPLIT_ = false>
 struct GemmCfg {
   static constexpr int BM = BM_, BNZ = BNZ_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, MF = MF_;
   static constexpr bool FP8 = FP8_, GATED = GATED_;
@@ -60,6 +60,12 @@ struct GemmCfg {
   static constexpr int NSTAGE = NSTAGE_;
   // Bytes of K per row in one k-tile: 128, or 64 (bf16 only).
   static constexpr int RB = RB_;
+  // Split rings: the activation rows (A) in a ring of 2 k-tiles, the weight
+  // rows (B) in a ring of 3, so two k-tiles of weight loads are in flight
+  // while one is consumed (weights stream from HBM; activation rows are
+  // re-read by every column tile and mostly come from L2).  NSTAGE is
+  // unused then.
+  static constexpr bool SPLIT = SPLIT_;
 };
 
 // gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16 lanes per
@@ -199,6 +205,35 @@ __device__ __forceinline__ void wait_vm_loads_but() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// LDS of one tile: the k-tile stages (or split rings), reused by the
+// epilogue's staging, then (fp8 only) the activation-scale table and the
+// tile's weight-block scales along K (sW: gate row, then up row).  bf16
+// tiles use every byte of the 160 KB for stages.
+template <class C>
+struct GemmLds {
+  static constexpr int G = C::GATED ? 2 : 1;
+  static constexpr int NB = G * C::BNZ;
+  static constexpr int A_BYTES = C::BM * C::RB, B_BYTES = NB * C::RB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int EPI_BYTES = (C::EPI == EPI_Z && C::FP8) ? C::BM * C::BNZ * 4 : C::BM * C::BNZ * 2;
+  static constexpr int ARING = 2, BRING = 3;
+  static constexpr int RING_BYTES = C::SPLIT ? ARING * A_BYTES + BRING * B_BYTES : C::NSTAGE * STAGE;
+  static constexpr int SMEM_TILE = cmax(RING_BYTES, EPI_BYTES);
+  static constexpr int kMaxKB = 128;  // K <= 16384
+  // Activation scales: the tile's whole table [k-tile][row] when its
+  // k-tiles fit SA_KB (loaded once before the k-loop), else two k-tiles in
+  // turn.  SA_KB (2..64) takes what the LDS leaves without lowering the
+  // number of workgroups per CU that the tile had with two k-tiles of
+  // scales.
+  static constexpr int kLds = 163840;
+  static constexpr int BASE_BYTES = SMEM_TILE + (C::FP8 ? (2 * C::BM + 2 * kMaxKB) * 4 : 0);
+  static constexpr int PER_WG = BASE_BYTES > kLds ? kLds : kLds / (kLds / BASE_BYTES);
+  static constexpr int SA_FIT = (PER_WG - SMEM_TILE - 2 * kMaxKB * 4) / (C::BM * 4);
+  static constexpr int SA_KB = !C::FP8 ? 2 : (SA_FIT < 2 ? 2 : (SA_FIT > 64 ? 64 : SA_FIT));
+  static constexpr int SCALE_BYTES = C::FP8 ? (SA_KB * C::BM + 2 * kMaxKB) * 4 : 0;
+  static_assert(SMEM_TILE + SCALE_BYTES <= kLds, "tile exceeds the LDS");
+};
+
 // Occupancy hint: the fp8 second-GEMM tile of 128 rows (64 KB of LDS) is
 // held to 128 VGPRs so that two workgroups share a CU, one's prologue and
 // epilogue overlapping the other's k-loop (its k-loop is only K/128 = 16
@@ -238,22 +273,19 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   constexpr int EPI_BYTES = (C::EPI == EPI_Z && FP8) ? BM * BNZ * 4 : BM * BNZ * 2;
   constexpr int NSTAGE = C::NSTAGE;
   static_assert(NSTAGE == 2 || (!FP8 && NI % NW == 0), "deeper pipelines: bf16, whole load groups");
-  constexpr int SMEM_TILE = cmax(NSTAGE * STAGE, EPI_BYTES);
-  // fp8 only, after the stages: the activation scales of two k-tiles
-  // (sA: this one and the next) and the tile's weight-block scales along K
-  // (sW: gate row, then up row).  bf16 tiles use every byte of the 160 KB
-  // for stages.
-  constexpr int kMaxKB = 128;  // K <= 16384
-  // Activation scales: the tile's whole table [k-tile][row] when its k-tiles
-  // fit SA_KB (loaded once before the k-loop), else two k-tiles in turn.
-  // SA_KB (2..64) takes what the LDS leaves without lowering the number of
-  // workgroups per CU that the tile had with two k-tiles of scales.
-  constexpr int kLds = 163840;
-  constexpr int BASE_BYTES = SMEM_TILE + (2 * BM + 2 * kMaxKB) * 4;
-  constexpr int PER_WG = kLds / (kLds / BASE_BYTES);
-  constexpr int SA_FIT = (PER_WG - SMEM_TILE - 2 * kMaxKB * 4) / (BM * 4);
-  constexpr int SA_KB = !FP8 ? 2 : (SA_FIT < 2 ? 2 : (SA_FIT > 64 ? 64 : SA_FIT));
-  constexpr int SCALE_BYTES = FP8 ? (SA_KB * BM + 2 * kMaxKB) * 4 : 0;
+  constexpr bool SPLIT = C::SPLIT;
+  static_assert(!SPLIT || NSTAGE == 2, "split rings replace the stage count");
+  constexpr int A_G = BM / RPG, B_G = NB / RPG;          // 1 KB load groups of A and of B rows
+  constexpr int NIA = (A_G + NW - 1) / NW, NIB = (B_G + NW - 1) / NW;
+  static_assert(!SPLIT || (B_G % NW == 0 && BM % RPG == 0),
+                "split rings: every wave issues the same number of weight loads");
+  typedef GemmLds<C> LDS;
+  constexpr int ARING = LDS::ARING, BRING = LDS::BRING;
+  constexpr int SMEM_TILE = LDS::SMEM_TILE;
+  static_assert(SMEM_TILE >= cmax(LDS::RING_BYTES, EPI_BYTES), "LDS layout");
+  constexpr int kMaxKB = LDS::kMaxKB;
+  constexpr int SA_KB = LDS::SA_KB;
+  constexpr int SCALE_BYTES = LDS::SCALE_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_TILE + SCALE_BYTES];
   float* const sA = reinterpret_cast<float*>(smem + SMEM_TILE);
   float* const sW = sA + SA_KB * BM;
@@ -324,37 +356,55 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   }
 
   // ---- direct-to-LDS source pointers ----
+  // Row r of a stage (A rows 0..BM-1, then B rows) and where it starts in
+  // global memory.
+  auto row_src = [&](int r) -> const uint8_t* {
+    if (r < BM) {
+      int srow = 0;
+      if constexpr (C::AMODE == A_GATHER) {
+        const int sid = p.sorted[m0 + r];
+        srow = sid < nflat ? sid / p.top_k : 0;   // pad rows read token 0 (discarded)
+      } else if constexpr (C::AMODE == A_ROWS) {
+        srow = m0 + r;
+      } else {
+        srow = min(m0 + r, p.T - 1);
+      }
+      return p.a + static_cast<int64_t>(srow) * krow_bytes;
+    }
+    const int b = r - BM;
+    int wrow;
+    if constexpr (C::GATED) wrow = b < BNZ ? n0 + b : p.inter + n0 + (b - BNZ);
+    else wrow = n0 + b;
+    return wbase + static_cast<int64_t>(wrow) * krow_bytes;
+  };
   // Load group j covers LDS rows RPG*j.. of a stage; lane i fills the
   // 16-byte slot i of the group, i.e. row RPG*j + i/LPR at physical chunk
-  // i%LPR, which holds logical chunk (i%LPR) ^ swz_key(row).
-  const uint8_t* src[NIW];
+  // i%LPR, which holds logical chunk (i%LPR) ^ swz_key(row).  (The key of
+  // a row depends on its index mod 16 only, and BM is a multiple of 16, so
+  // B rows have the same key whether counted from the stage or from B.)
+  const uint8_t* src[SPLIT ? 1 : NIW];
+  const uint8_t* srcA[SPLIT ? NIA : 1];
+  const uint8_t* srcB[SPLIT ? NIB : 1];
+  if constexpr (!SPLIT) {
 #pragma unroll
-  for (int s = 0; s < NIW; ++s) {
-    const int j = wave + NW * s;
-    const int r = RPG * j + lane / LPR;
-    const int lchunk = (lane % LPR) ^ swz_key<RB>(r);
-    const uint8_t* ptr = p.a;  // any valid row; unused when j >= NI
-    if (j < NI) {
-      if (r < BM) {
-        int srow = 0;
-        if constexpr (C::AMODE == A_GATHER) {
-          const int sid = p.sorted[m0 + r];
-          srow = sid < nflat ? sid / p.top_k : 0;   // pad rows read token 0 (discarded)
-        } else if constexpr (C::AMODE == A_ROWS) {
-          srow = m0 + r;
-        } else {
-          srow = min(m0 + r, p.T - 1);
-        }
-        ptr = p.a + static_cast<int64_t>(srow) * krow_bytes;
-      } else {
-        const int b = r - BM;
-        int wrow;
-        if constexpr (C::GATED) wrow = b < BNZ ? n0 + b : p.inter + n0 + (b - BNZ);
-        else wrow = n0 + b;
-        ptr = wbase + static_cast<int64_t>(wrow) * krow_bytes;
-      }
+    for (int s = 0; s < NIW; ++s) {
+      const int j = wave + NW * s;
+      const int r = RPG * j + lane / LPR;
+      const int lchunk = (lane % LPR) ^ swz_key<RB>(r);
+      src[s] = (j < NI ? row_src(r) : p.a) + lchunk * 16;   // p.a: any valid row, unused
     }
-    src[s] = ptr + lchunk * 16;
+  } else {
+#pragma unroll
+    for (int s = 0; s < NIA; ++s) {
+      const int a = wave + NW * s;
+      const int r = RPG * a + lane / LPR;
+      srcA[s] = (a < A_G ? row_src(r) : p.a) + ((lane % LPR) ^ swz_key<RB>(r)) * 16;
+    }
+#pragma unroll
+    for (int s = 0; s < NIB; ++s) {
+      const int rb = RPG * (wave + NW * s) + lane / LPR;
+      srcB[s] = row_src(BM + rb) + ((lane % LPR) ^ swz_key<RB>(rb)) * 16;
+    }
   }
   // fp8: this thread's activation-scale row (threads < BM) and the weight-scale rows
   static_assert(!FP8 || BM <= NT, "one activation-scale row per thread");
@@ -395,6 +445,8 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   // 256-row block saves a quarter of its loads.  The count of loads in
   // flight then varies by wave, so this needs the two-stage loop, which
   // waits for all of them (vmcnt(0)).  Full tiles keep branch-free loads.
+  // With split rings the weight loads alone are counted by the waits, so
+  // the activation loads may be skipped as well.
   const int a_groups = (NSTAGE == 2) ? (valid_rows + RPG - 1) / RPG : BM / RPG;
   auto dma = [&](int kt, int buf, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
@@ -405,6 +457,24 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       if ((NI % NW == 0 || j < NI) && (FULL || j >= BM / RPG || j < a_groups))
         lds_dma16(src[s] + static_cast<int64_t>(kt) * RB, smem + buf * STAGE + j * 1024);
     }
+  };
+  // split rings: A k-tile kt into A buffer buf, B k-tile kt into B buffer buf
+  auto dma_a = [&](int kt, int buf, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    kt += kbase;
+#pragma unroll
+    for (int s = 0; s < NIA; ++s) {
+      const int a = wave + NW * s;
+      if ((A_G % NW == 0 || a < A_G) && (FULL || a < a_groups))
+        lds_dma16(srcA[s] + static_cast<int64_t>(kt) * RB, smem + buf * A_BYTES + a * 1024);
+    }
+  };
+  auto dma_b = [&](int kt, int buf) {
+    kt += kbase;
+#pragma unroll
+    for (int s = 0; s < NIB; ++s)
+      lds_dma16(srcB[s] + static_cast<int64_t>(kt) * RB,
+                smem + ARING * A_BYTES + buf * B_BYTES + (wave + NW * s) * 1024);
   };
 
 
@@ -423,209 +493,286 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   const int fm_live = __builtin_amdgcn_readfirstlane(
       valid_rows > row_w ? min(FM, (valid_rows - row_w + MF - 1) / MF) : 0);
 
-  // fp8 k-loop.  A k-tile is one 128-deep scale block: its MFMAs sum into a
+  // fp8 k-tiles.  A k-tile is one 128-deep scale block: its MFMAs sum into a
   // fresh partial, which is promoted into the fp32 accumulator as
   // acc += partial * s_a[row] * s_w.  The k-tile's activation scales are
   // read from LDS (16-byte reads: an accumulator's rows come in runs of 4)
   // right after the barrier, so their latency hides behind the MFMAs.
   // The rows' scales reach LDS as one [k-tile][row] table per tile, loaded
-  // before the loop; when the table does not fit, by a direct-to-LDS load
-  // per k-tile issued with the stage loads.  Either way no load into a
-  // register is in flight inside the loop.  (Loaded into a register and
-  // stored to LDS at the end of each iteration, the scale made the compiler
-  // wait for vmcnt(0) inside the iteration -- loads complete in order --
-  // which also drained the next k-tile's stage loads: 12 % of the gated
-  // first GEMM's time at DeepSeek-V3 T=8192.)
+  // before the loop; when the table does not fit (two-stage ring only), by
+  // a direct-to-LDS load per k-tile issued with the stage loads.  Either way
+  // no load into a register is in flight inside the loop.  (Loaded into a
+  // register and stored to LDS at the end of each iteration, the scale made
+  // the compiler wait for vmcnt(0) inside the iteration -- loads complete in
+  // order -- which also drained the next k-tile's stage loads: 12 % of the
+  // gated first GEMM's time at DeepSeek-V3 T=8192.)
   // (Deferring each promotion by one k-tile with two partial sets was
   // measured slower: the extra registers cost occupancy.)
-  auto kloop_fp8 = [&](auto full_tag) {
+  // Whole table when it fits; split rings always fit it (the host only
+  // picks a split-ring tile when K / 128 / ksplit <= its capacity).
+  const bool whole = SPLIT || nk <= SA_KB;
+  // Row r's scale of k-tile kt straight to sA[kt & 1][r] by a 4-byte
+  // direct-to-LDS load (threads r < BM; lane i of a wave writes 4*i bytes
+  // past the wave's base), issued with the k-tile's stage loads.
+  auto dma_sa = [&](int kt, int b) {
+    if (tid < BM) {
+      typedef __attribute__((address_space(3))) void lds_void;
+      const float* g = p.a_scale + static_cast<int64_t>(a_srow) * p.sa_row +
+                       static_cast<int64_t>(kbase + kt) * p.sa_k;
+      __builtin_amdgcn_global_load_lds(g, (lds_void*)(sA + b * BM + (tid & ~63)), 4, 0, 0);
+    }
+  };
+  // Whole table: thread r < BM loads its row's scales of this tile's
+  // k-tiles (16-byte loads where the row's G(128) scales are contiguous and
+  // aligned) and stores them to sA[kt][r]; the first barrier publishes them.
+  // The loads are consumed here, before the loop, so none is in flight into
+  // a register when it starts.
+  auto load_scale_table = [&]() {
+    if (!(whole && tid < BM)) return;
+    // batches of up to 8 loads in flight before their stores (the first
+    // k-tiles' stage loads are already under way)
+    const float* g = p.a_scale + static_cast<int64_t>(a_srow) * p.sa_row +
+                     static_cast<int64_t>(kbase) * p.sa_k;
+    int kv = 0;   // scales taken by whole 16-byte loads (never past k-tile nk-1)
+    if (p.sa_k == 1 && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+      kv = nk & ~3;
+      for (int k0 = 0; k0 < kv; k0 += 32) {
+        f32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (k0 + 4 * j < kv) v[j] = *reinterpret_cast<const f32x4*>(g + k0 + 4 * j);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (k0 + 4 * j < kv) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sA[(k0 + 4 * j + i) * BM + tid] = v[j][i];
+          }
+      }
+    }
+    for (int k0 = kv; k0 < nk; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < nk) v[j] = g[static_cast<int64_t>(k0 + j) * p.sa_k];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < nk) sA[(k0 + j) * BM + tid] = v[j];
+    }
+  };
+
+  // One fp8 k-tile (kt, tile-local) from stage buffers As / Bs.
+  auto compute_fp8 = [&](int kt, const uint8_t* As, const uint8_t* Bs, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    static_assert(!FP8 || NSTAGE == 2, "fp8 runs two LDS stages");
-    // Whole table: thread r < BM loads its row's scales of this tile's
-    // k-tiles (16-byte loads where the row's G(128) scales are contiguous and
-    // aligned) and stores them to sA[kt][r]; the first barrier publishes
-    // them.  The loads are consumed here, before the loop, so none is in
-    // flight into a register when it starts.
-    const bool whole = nk <= SA_KB;
-    // Otherwise row r's scale of k-tile kt goes straight to sA[kt & 1][r] by
-    // a 4-byte direct-to-LDS load (threads r < BM; lane i of a wave writes 4*i
-    // bytes past the wave's base), issued with the k-tile's stage loads.
-    auto dma_sa = [&](int kt, int b) {
-      if (tid < BM) {
-        typedef __attribute__((address_space(3))) void lds_void;
-        const float* g = p.a_scale + static_cast<int64_t>(a_srow) * p.sa_row +
-                         static_cast<int64_t>(kbase + kt) * p.sa_k;
-        __builtin_amdgcn_global_load_lds(g, (lds_void*)(sA + b * BM + (tid & ~63)), 4, 0, 0);
+    // this k-tile's scales: weight blocks (gate, up) and the rows' activation
+    // scales; the latter are read ahead of the MFMAs unless registers are
+    // held to 128 for occupancy (LEAN), then inside the promotion
+    constexpr bool LEAN = gemm_min_waves_per_eu<C>() > 1;
+    constexpr bool PER_FRAGMENT = BM >= 256;
+    const float swg[2] = {sW[wblk * kMaxKB + kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
+    const float* sAb = sA + (whole ? kt : (kt & 1)) * BM;
+    auto read_sa = [&](int fm, float (&out)[NACC]) {
+#pragma unroll
+      for (int q = 0; q < NACC / 4; ++q) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(sAb + row_w + fm * MF + acc_row<MF>(4 * q, lane));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[4 * q + r] = t[r];
       }
     };
-    if (nk > 0) {
-      if (!whole) dma_sa(0, 0);
-      dma(0, 0, full_tag);
-    }
-    if (whole && tid < BM) {
-      // batches of up to 8 loads in flight before their stores (the first
-      // k-tile's stage loads are already under way)
-      const float* g = p.a_scale + static_cast<int64_t>(a_srow) * p.sa_row +
-                       static_cast<int64_t>(kbase) * p.sa_k;
-      int kv = 0;   // scales taken by whole 16-byte loads (never past k-tile nk-1)
-      if (p.sa_k == 1 && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
-        kv = nk & ~3;
-        for (int k0 = 0; k0 < kv; k0 += 32) {
-          f32x4 v[8];
+    if constexpr (PER_FRAGMENT) {
+      // 256-row tiles: each row fragment's partial is summed and promoted
+      // before the next one starts, so only one fragment's partial set is
+      // live beside the accumulators (a full partial set would double them).
+      frag_t fb[NSUB][G][FN];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (k0 + 4 * j < kv) v[j] = *reinterpret_cast<const f32x4*>(g + k0 + 4 * j);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (k0 + 4 * j < kv) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) sA[(k0 + 4 * j + i) * BM + tid] = v[j][i];
-            }
-        }
-      }
-      {
-        for (int k0 = kv; k0 < nk; k0 += 8) {
-          float v[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (k0 + j < nk) v[j] = g[static_cast<int64_t>(k0 + j) * p.sa_k];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (k0 + j < nk) sA[(k0 + j) * BM + tid] = v[j];
-        }
-      }
-    }
-    int buf = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-      // k-tile kt's loads (stage and scales) have landed
-      wait_vm_loads();
-      lds_barrier();
-      if (kt + 1 < nk) {
-        // buffer (kt+1)&1 was last read in iteration kt-1, before this barrier
-        if (!whole) dma_sa(kt + 1, (kt + 1) & 1);
-        dma(kt + 1, buf ^ 1, full_tag);
-      }
-      // this k-tile's scales: weight blocks (gate, up) and the rows' activation
-      // scales; the latter are read ahead of the MFMAs unless registers are
-      // held to 128 for occupancy (LEAN), then inside the promotion
-      constexpr bool LEAN = gemm_min_waves_per_eu<C>() > 1;
-      constexpr bool PER_FRAGMENT = BM >= 256;
-      const float swg[2] = {sW[wblk * kMaxKB + kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
-      const float* sAb = sA + (whole ? kt : (kt & 1)) * BM;
-      auto read_sa = [&](int fm, float (&out)[NACC]) {
-#pragma unroll
-        for (int q = 0; q < NACC / 4; ++q) {
-          const f32x4 t = *reinterpret_cast<const f32x4*>(sAb + row_w + fm * MF + acc_row<MF>(4 * q, lane));
-#pragma unroll
-          for (int r = 0; r < 4; ++r) out[4 * q + r] = t[r];
-        }
-      };
-      float sa[(LEAN || PER_FRAGMENT) ? 1 : FM][NACC];
-      if constexpr (!LEAN && !PER_FRAGMENT) {
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) read_sa(fm, sa[fm]);
-      }
-      const uint8_t* As = smem + buf * STAGE;
-      const uint8_t* Bs = As + A_BYTES;
-      if constexpr (PER_FRAGMENT) {
-        // 256-row tiles: each row fragment's partial is summed and promoted
-        // before the next one starts, so only one fragment's partial set is
-        // live beside the accumulators (a full partial set would double them).
-        frag_t fb[NSUB][G][FN];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-              fb[s][g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          if (!(FULL || fm < fm_live)) continue;
-          acc_t pf[G][FN];
-#pragma unroll
-          for (int s = 0; s < NSUB; ++s) {
-            const frag_t fa = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-              for (int fn = 0; fn < FN; ++fn) {
-                if (s == 0) {
-#pragma unroll
-                  for (int v = 0; v < NACC; ++v) pf[g][fn][v] = 0.f;
-                }
-                pf[g][fn] = M::mma(fa, fb[s][g][fn], pf[g][fn]);
-              }
-          }
-          float sr[NACC];
-          read_sa(fm, sr);
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-              for (int v = 0; v < NACC; ++v)
-                acc[g][fm][fn][v] += pf[g][fn][v] * (sr[v] * swg[g]);
-        }
-        buf ^= 1;
-        continue;
-      }
-      acc_t part[G][FM][FN];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        frag_t fa[FM], fb[G][FN];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-          if (FULL || fm < fm_live) fa[fm] = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+      for (int s = 0; s < NSUB; ++s)
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
-            fb[g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-          if (FULL || fm < fm_live)
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-              for (int fn = 0; fn < FN; ++fn) {
-                if (s == 0) {
-#pragma unroll
-                  for (int v = 0; v < NACC; ++v) part[g][fm][fn][v] = 0.f;
-                }
-                part[g][fm][fn] = M::mma(fa[fm], fb[g][fn], part[g][fm][fn]);
-              }
-      }
+            fb[s][g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         if (!(FULL || fm < fm_live)) continue;
-        const float* sr = sa[0];
-        float lean[NACC];
-        if constexpr (LEAN) {
-          read_sa(fm, lean);
-          sr = lean;
-        } else {
-          sr = sa[fm];
+        acc_t pf[G][FN];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          const frag_t fa = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+              if (s == 0) {
+#pragma unroll
+                for (int v = 0; v < NACC; ++v) pf[g][fn][v] = 0.f;
+              }
+              pf[g][fn] = M::mma(fa, fb[s][g][fn], pf[g][fn]);
+            }
         }
+        float sr[NACC];
+        read_sa(fm, sr);
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
             for (int v = 0; v < NACC; ++v)
-              acc[g][fm][fn][v] += part[g][fm][fn][v] * (sr[v] * swg[g]);
+              acc[g][fm][fn][v] += pf[g][fn][v] * (sr[v] * swg[g]);
       }
-      buf ^= 1;
+      return;
     }
+    float sa[(LEAN || PER_FRAGMENT) ? 1 : FM][NACC];
+    if constexpr (!LEAN && !PER_FRAGMENT) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) read_sa(fm, sa[fm]);
+    }
+    acc_t part[G][FM][FN];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      frag_t fa[FM], fb[G][FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        if (FULL || fm < fm_live) fa[fm] = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          fb[g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        if (FULL || fm < fm_live)
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+              if (s == 0) {
+#pragma unroll
+                for (int v = 0; v < NACC; ++v) part[g][fm][fn][v] = 0.f;
+              }
+              part[g][fm][fn] = M::mma(fa[fm], fb[g][fn], part[g][fm][fn]);
+            }
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (!(FULL || fm < fm_live)) continue;
+      const float* sr = sa[0];
+      float lean[NACC];
+      if constexpr (LEAN) {
+        read_sa(fm, lean);
+        sr = lean;
+      } else {
+        sr = sa[fm];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int v = 0; v < NACC; ++v)
+            acc[g][fm][fn][v] += part[g][fm][fn][v] * (sr[v] * swg[g]);
+    }
+  };
+
+  // One bf16 k-tile from stage buffers As / Bs.  Two fragment sets:
+  // substep s+1's LDS reads are in flight while substep s's MFMAs issue
+  // (interleaved by sched_group_barrier).
+  auto compute_bf16 = [&](const uint8_t* As, const uint8_t* Bs, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    frag_t fa[2][FM], fb[2][G][FN];
+    auto rd = [&](int s, int set) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        if (FULL || fm < fm_live)
+          fa[set][fm] = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          fb[set][g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < NSUB) rd(s + 1, cur ^ 1);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        if (FULL || fm < fm_live)
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              acc[g][fm][fn] = M::mma(fa[cur][fm], fb[cur][g][fn], acc[g][fm][fn]);
+      if constexpr (FULL) {
+        if (s + 1 < NSUB) {
+          constexpr int NR = FM + G * FN, NMM = G * FM * FN;
+          constexpr int PER = NMM / NR > 0 ? NMM / NR : 1;
+#pragma unroll
+          for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, NMM - PER * NR > 0 ? NMM - PER * NR : 0, 0);
+        }
+      }
+    }
+  };
+
+  auto compute = [&](int kt, const uint8_t* As, const uint8_t* Bs, auto full_tag) {
+    if constexpr (FP8) compute_fp8(kt, As, Bs, full_tag);
+    else compute_bf16(As, Bs, full_tag);
   };
 
   // The k-loop, instantiated twice: branch-free when every fragment row
   // block holds data (all but an expert's last block), and with uniform
   // per-fragment guards otherwise.
   auto kloop = [&](auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
+    if constexpr (SPLIT) {
+      // Loads issue in the order B(0) A(0) B(1) | A(1) B(2) | A(2) B(3) ...
+      // (iteration kt issues A(kt+1), then B(kt+2)).  At the top of
+      // iteration kt the only loads of this wave that may still be in flight
+      // are B(kt+1)'s NIB (issued after A(kt) and B(kt)), and loads complete
+      // in order, so vmcnt(NIB) means A(kt) and B(kt) have landed.  The
+      // barrier then also guarantees that every wave has finished reading
+      // A buffer (kt+1)&1 and B buffer (kt+2)%3, last read in iteration kt-1.
+      if (nk > 0) {
+        dma_b(0, 0);
+        dma_a(0, 0, full_tag);
+      }
+      if (nk > 1) dma_b(1, 1);
+      if constexpr (FP8) load_scale_table();
+      int bb = 0;
+      for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk) wait_vm_loads_but<NIB>();
+        else wait_vm_loads();
+        lds_barrier();
+        const int bn2 = bb + 2 >= BRING ? bb + 2 - BRING : bb + 2;
+        if (kt + 1 < nk) dma_a(kt + 1, (kt + 1) & 1, full_tag);
+        if (kt + 2 < nk) dma_b(kt + 2, bn2);
+        compute(kt, smem + (kt & 1) * A_BYTES, smem + ARING * A_BYTES + bb * B_BYTES, full_tag);
+        bb = bb + 1 == BRING ? 0 : bb + 1;
+      }
+      return;
+    }
     if constexpr (FP8) {
-      kloop_fp8(full_tag);
+      static_assert(!FP8 || NSTAGE == 2, "fp8 runs two LDS stages");
+      if (nk > 0) {
+        if (!whole) dma_sa(0, 0);
+        dma(0, 0, full_tag);
+      }
+      load_scale_table();
+      int buf = 0;
+      for (int kt = 0; kt < nk; ++kt) {
+        // k-tile kt's loads (stage and scales) have landed
+        wait_vm_loads();
+        lds_barrier();
+        if (kt + 1 < nk) {
+          // buffer (kt+1)&1 was last read in iteration kt-1, before this barrier
+          if (!whole) dma_sa(kt + 1, (kt + 1) & 1);
+          dma(kt + 1, buf ^ 1, full_tag);
+        }
+        compute(kt, smem + buf * STAGE, smem + buf * STAGE + A_BYTES, full_tag);
+        buf ^= 1;
+      }
       return;
     }
 #pragma unroll
@@ -644,50 +791,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       }
       lds_barrier();
       if (kt + NSTAGE - 1 < nk) dma(kt + NSTAGE - 1, nbuf, full_tag);
-      const uint8_t* As = smem + buf * STAGE;
-      const uint8_t* Bs = As + A_BYTES;
-      {
-        // Two fragment sets: substep s+1's LDS reads are in flight while
-        // substep s's MFMAs issue (interleaved by sched_group_barrier).
-        frag_t fa[2][FM], fb[2][G][FN];
-        auto rd = [&](int s, int set) {
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-            if (FULL || fm < fm_live)
-              fa[set][fm] = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-              fb[set][g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
-        };
-        rd(0, 0);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          const int cur = s & 1;
-          if (s + 1 < NSUB) rd(s + 1, cur ^ 1);
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-            if (FULL || fm < fm_live)
-#pragma unroll
-              for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                  acc[g][fm][fn] = M::mma(fa[cur][fm], fb[cur][g][fn], acc[g][fm][fn]);
-          if constexpr (FULL) {
-            if (s + 1 < NSUB) {
-              constexpr int NR = FM + G * FN, NMM = G * FM * FN;
-              constexpr int PER = NMM / NR > 0 ? NMM / NR : 1;
-#pragma unroll
-              for (int i = 0; i < NR; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
-              }
-              __builtin_amdgcn_sched_group_barrier(0x008, NMM - PER * NR > 0 ? NMM - PER * NR : 0, 0);
-            }
-          }
-        }
-      }
+      compute(kt, smem + buf * STAGE, smem + buf * STAGE + A_BYTES, full_tag);
       buf = buf + 1 == NSTAGE ? 0 : buf + 1;
       nbuf = nbuf + 1 == NSTAGE ? 0 : nbuf + 1;
     }

@@ -60,6 +60,10 @@ struct GemmParams {
   float* partial;
   int64_t part_rows;
   int ldp;
+  // Weight rows through a 3-deep ring where a tile exists for it
+  // (GemmCfg::SPLIT): set for the routed bf16 GEMMs, whose 256-row tiles
+  // stream weights with little reuse at medium T.
+  int split_ring;
 };
 
 enum ActFn { ACT_SILU = 0, ACT_GELU = 1 };

@@ -353,8 +353,15 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
     else (void)launch_gemm_bf16(kind, gated, blk_m, bnz, &p, max_mblk, s);
   };
   const int act = act_fn(activation);
+  // Weight rows through the 3-deep ring (routed launches whose experts
+  // average at most one block of rows: each weight tile then serves one
+  // block and its loads stream from HBM; measured 9-10 % faster there,
+  // 2 % slower at Mixtral T=4096 with four blocks per expert).
+  const int64_t touched_e = std::min<int64_t>(w->num_experts, std::max<int64_t>(nflat, 1));
+  const bool stream_rows = nflat <= touched_e * bm;
   auto split = [&](GemmParams& g, int S, int64_t part_rows, int ldp) {
     g.act = act;
+    g.split_ring = (g.sorted != nullptr && stream_rows) ? 1 : 0;
     g.ksplit = S;
     g.partial = S > 1 ? part : nullptr;
     g.part_rows = part_rows;

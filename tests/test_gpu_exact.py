@@ -89,6 +89,9 @@ EXACT_SHAPES = [
     dict(name="exact_small", T=61, H=384, I=256, E=4, top_k=2, shared_I=256),
     # decode-sized, long K: the GEMMs split K
     dict(name="exact_split", T=3, H=2048, I=1024, E=4, top_k=2, shared_I=1024),
+    # several 256-row blocks per expert: the bf16 256-row tiles on two stages
+    # (fewer rows per expert take the 3-deep weight ring)
+    dict(name="exact_tall", T=700, H=256, I=128, E=2, top_k=1, shared_I=128),
 ]
 
 
