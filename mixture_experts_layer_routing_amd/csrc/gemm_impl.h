@@ -34,9 +34,11 @@
 // fp32 accumulator as acc += partial * s_a[row] * s_w[block].
 //
 // Tile order: workgroups are dealt to the 8 XCDs round-robin; each XCD gets
-// a contiguous range of tiles in a grouped order (8 M-blocks down, then the
-// next N-tile), so the workgroups resident on one XCD share activation rows
-// and weight tiles through that XCD's L2.
+// a contiguous range of tiles in a grouped order -- expert-major (one
+// expert's M-blocks down, then the next N-tile) when the align offsets are
+// given, else 8 M-blocks down, then the next N-tile -- so the workgroups
+// resident on one XCD share activation rows and weight tiles through that
+// XCD's L2.
 #pragma once
 
 #include <type_traits>
@@ -312,13 +314,28 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   if (jj >= per) return;
   const int logical = (bid & 7) * per + jj;
   if (logical >= total) return;
-  constexpr int GM = 8;
-  const int grp = logical / (GM * p.n_tiles);
-  const int first_m = grp * GM;
-  const int gm = min(n_mblk - first_m, GM);
-  const int rem = logical - grp * GM * p.n_tiles;
-  const int mblk = first_m + rem % gm;
-  const int ntile = rem / gm;
+  int mblk, ntile;
+  if (C::AMODE != A_DENSE && p.expert_offsets != nullptr) {
+    // Expert-major order: the tiles of one expert are consecutive, its
+    // M-blocks fastest, so the tiles resident on an XCD at once share the
+    // expert's weight tiles (and its activation rows) in that XCD's L2.
+    // Expert e owns tiles [b0 * n_tiles, b1 * n_tiles) with b0, b1 its first
+    // and end M-block, so M-block logical / n_tiles is one of e's blocks.
+    const int e = p.block_expert[(logical / p.n_tiles) * BM / p.align_bm];
+    const int b0 = p.expert_offsets[e] / BM, nb = p.expert_offsets[e + 1] / BM - b0;
+    const int rem = logical - b0 * p.n_tiles;
+    mblk = b0 + rem % nb;
+    ntile = rem / nb;
+  } else {
+    // groups of GM M-blocks (8 down, then the next N-tile)
+    constexpr int GM = 8;
+    const int grp = logical / (GM * p.n_tiles);
+    const int first_m = grp * GM;
+    const int gm = min(n_mblk - first_m, GM);
+    const int rem = logical - grp * GM * p.n_tiles;
+    mblk = first_m + rem % gm;
+    ntile = rem / gm;
+  }
   const int m0 = mblk * BM, n0 = ntile * BNZ;
 
   const uint8_t* wbase = p.w;

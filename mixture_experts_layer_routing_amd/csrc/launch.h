@@ -45,6 +45,8 @@ struct GemmParams {
   const int32_t* sorted;   // align outputs (routed launches)
   const int32_t* block_expert;
   const int32_t* ntp;
+  const int32_t* expert_offsets;   // align's padded offsets [E+1] (rows), or null:
+                                   // then the tile order ignores expert boundaries
   int T, top_k;
   int align_bm;            // align block size (routed launches); a multiple of the tile BM
   void* out;               // z / fused_expert_output / shared_out

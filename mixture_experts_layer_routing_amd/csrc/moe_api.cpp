@@ -331,8 +331,8 @@ int tiles_exist(int T, int H, const moe_weights* w, int activation, int bm) {
 int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
                 const float* shared_in_scale, const Routed& rt, int T, int H, const moe_weights* w,
                 int activation, const int32_t* sorted, const int32_t* block_expert,
-                const int32_t* ntp, int bm, uint16_t* feo, uint16_t* shared_out, void* ws,
-                const StageEvents& se, hipStream_t s) {
+                const int32_t* ntp, const int32_t* offsets, int bm, uint16_t* feo,
+                uint16_t* shared_out, void* ws, const StageEvents& se, hipStream_t s) {
   using namespace moe;
   const bool fp8 = quant_fp8(w->quant);
   const bool gated = act_gated(activation);
@@ -384,6 +384,7 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   p.sorted = sorted;
   p.block_expert = block_expert;
   p.ntp = ntp;
+  p.expert_offsets = offsets;
   p.T = rt.T;
   p.top_k = rt.top_k;
   p.align_bm = bm;
@@ -413,6 +414,7 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   q.sorted = sorted;
   q.block_expert = block_expert;
   q.ntp = ntp;
+  q.expert_offsets = offsets;
   q.T = rt.T;
   q.top_k = rt.top_k;
   q.align_bm = bm;
@@ -635,9 +637,9 @@ int moe_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   if (int st = tiles_exist(T, H, weights, activation, block_m)) return st;
   return run_experts(a1q, a1q_scale, shared_in, shared_in_scale,
                      standard_rows(T, top_k, weights->num_experts, block_m), T, H, weights,
-                     activation, sorted_token_ids, block_expert_ids, num_tokens_post_padded, block_m,
-                     fused_expert_output, shared_out, workspace, StageEvents{nullptr, stream},
-                     stream);
+                     activation, sorted_token_ids, block_expert_ids, num_tokens_post_padded,
+                     nullptr, block_m, fused_expert_output, shared_out, workspace,
+                     StageEvents{nullptr, stream}, stream);
 }
 
 namespace {
@@ -740,7 +742,8 @@ int moe_experts_batched(const void* a, const float* a_scale, const int32_t* expe
                                L.blocks, L.ntp, stream);
   if (int st = check_launch("moe_experts_batched schedule")) return st;
   return run_experts(a, a_scale, nullptr, nullptr, rt, 0, H, &w, activation, L.sorted, L.blocks,
-                     L.ntp, bm, out, nullptr, L.experts_ws, StageEvents{nullptr, stream}, stream);
+                     L.ntp, nullptr, bm, out, nullptr, L.experts_ws, StageEvents{nullptr, stream},
+                     stream);
 }
 
 int moe_finalize(void* output, float* output_scale, int out_quant,
@@ -916,7 +919,8 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
                     cp.block_cap, L.ntp, L.align_ws, stream);
   se.mark(3);
   int st = run_experts(a1q, L.a1q_scale, shin, shin_scale, standard_rows(T, top_k, E, bm), T, H,
-                       weights, activation, L.sorted, L.blocks, L.ntp, bm, L.feo, L.shared_out, L.experts_ws, se, stream);
+                       weights, activation, L.sorted, L.blocks, L.ntp, L.offsets, bm, L.feo,
+                       L.shared_out, L.experts_ws, se, stream);
   if (st) return st;
   moe::launch_finalize(output, output_scale, out_quant, L.feo, L.tw, T, top_k, H,
                        apply_router_weight_on_input ? 1 : 0, L.shared_out, residual, residual_out,
