@@ -8,9 +8,12 @@ N(0, 2)) at T=4096 tokens.
 
 Prints ONE JSON line: tokens/s (value), TFLOP/s, per-stage times from HIP
 events recorded on the launch stream, the dominant kernel's roofline
-(routed GEMM-1, MFMA-bound), the memory-bound stages' bandwidth (finalize
-at hidden 7168 with a cold cache, align over 2^24 ids) and the CPU oracle
-timed on a bounded token sample on this host ("cpu_baseline").
+(routed GEMM-1, MFMA-bound), the layer's fraction of its roofline, a second
+leg on the fp8 path (the DeepSeek-V3-shaped layer at T=8192 by default:
+its own GEMM-1 roofline against the fp8 peak and the HBM floor), the
+memory-bound stages' bandwidth (finalize at hidden 7168 with a cold cache,
+align over 2^24 ids) and the CPU oracle timed on a bounded token sample on
+this host ("cpu_baseline").
 """
 
 import argparse
@@ -35,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral@T4096",
                     help="family@T<tokens>, e.g. mixtral@T4096, deepseek_v3@T8192, llama4@T2048")
     ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--fp8-leg", default="deepseek_v3@T8192",
+                    help="second workload timed in the same run (the fp8 path); 'none' to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay leg (counter passes profile eager launches only)")
@@ -150,6 +155,29 @@ def gemm1_flops(spec):
     return 2.0 * spec.T * spec.top_k * spec.H * spec.I * g
 
 
+def layer_roofline(spec, touched):
+    """The layer's roofline time: its algorithmic flops at the dense MFMA
+    peak of its dtype, or its algorithmic HBM bytes at 8 TB/s, whichever is
+    longer.  Bytes: the touched experts' weights (+ fp8 block scales) and
+    the shared expert's, read once; x read; a1q written and read; z written
+    and read; fused_expert_output written and read; the output written.
+    Padding rows are not counted."""
+    fp8 = spec.quant.startswith("fp8")
+    eb = 1 if fp8 else 2
+    g = 2 if spec.activation in ("silu", "gelu") else 1
+    H, I, Is, T, k = spec.H, spec.I, spec.shared_I, spec.T, spec.top_k
+    w = touched * (g * I * H + H * I) * eb + (g * Is * H + H * Is) * eb
+    if fp8:
+        w += 4 * (touched * (g * I * H + H * I) + (g * Is * H + H * Is)) // (128 * 128)
+    act = T * H * 2 + 2 * T * H * eb + 2 * (T * k * I + T * Is) * eb + 2 * T * k * H * 2 \
+        + T * H * 2
+    routed, shared = layer_flops(spec)
+    t_mfma = (routed + shared) / (PEAK_TFLOPS["fp8" if fp8 else "bf16"] * 1e12)
+    t_hbm = (w + act) / (PEAK_HBM_GBS * 1e9)
+    return {"ms": round(max(t_mfma, t_hbm) * 1e3, 4), "bound": "mfma" if t_mfma > t_hbm else "hbm",
+            "flops": routed + shared, "bytes": int(w + act), "touched_experts": int(touched)}
+
+
 def cpu_baseline(spec, d, sample_n):
     import numpy as np
     import oracle
@@ -174,9 +202,10 @@ def cpu_baseline(spec, d, sample_n):
                    res, gam, spec.eps, spec.out_quant, tokens=sample)
     dt = time.perf_counter() - t0
     return {"value": round(sample.size / dt, 3), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{sample.size} of {spec.T} tokens (route+align over all {spec.T}), "
-                      f"numpy float64, mirrored mode, {dt:.1f} s"}
+                      f"numpy float64, mirrored mode, {dt:.1f} s; cores = BLAS threads, "
+                      f"host_cpus = CPUs this process may run on"}
 
 
 def hbm_stages(torch, moe, dev):
@@ -252,27 +281,16 @@ def hbm_stages(torch, moe, dev):
     return out
 
 
-def main():
-    a = parse()
-    if a.write_traffic:
-        if a.copy_calibration <= 0:
-            raise SystemExit("--write-traffic needs --copy-calibration BYTES of the profiled run")
-        write_traffic(a)
-        return
-    if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(multi-GPU sharding is a design note, not implemented)"}))
-        sys.exit(2)
-    import torch
-    import mixture_experts_layer_routing_amd as moe
+def measure(a, torch, moe, spec, block_m=0, graph=True):
+    """Time one workload: K plain moe_forward steps (the headline), K steps
+    with stage events (per-stage times, GEMM-1's duration), and K replays
+    of the step as one graph launch.  Returns (result dict, inputs)."""
     from workloads import make_layer_inputs
-
-    spec = find_spec(a.workload)
     dev = "cuda"
     d = make_layer_inputs(spec, device=dev)
     w = moe.make_weights(*(d.get(k) for k in ("w13", "w2", "w13_scale", "w2_scale", "shared_w13",
                                               "shared_w2", "shared_w13_scale", "shared_w2_scale")))
-    bm = a.block_m or moe.moe_pick_block_m(spec.T, spec.top_k, spec.E, spec.quant)
+    bm = block_m or moe.moe_pick_block_m(spec.T, spec.top_k, spec.E, spec.quant)
     stream = torch.cuda.current_stream()
 
     def step(events=None, ws=None, out=None):
@@ -307,34 +325,76 @@ def main():
     # kernels and buffers are identical, only the per-kernel host submission
     # is gone -- the rate a decode loop sees
     graph_ms = None
-    if not a.no_graph:
+    if graph:
         gstream = torch.cuda.Stream()
         with torch.cuda.stream(gstream):
-            graph = moe.ForwardGraph(d["x"], d["logits"], w, spec.top_k, spec.scoring,
-                                     spec.renormalize, spec.apply_router_weight_on_input,
-                                     spec.activation, bm, d.get("residual"), d.get("gamma"),
-                                     spec.eps, spec.out_quant)
+            g = moe.ForwardGraph(d["x"], d["logits"], w, spec.top_k, spec.scoring,
+                                 spec.renormalize, spec.apply_router_weight_on_input,
+                                 spec.activation, bm, d.get("residual"), d.get("gamma"),
+                                 spec.eps, spec.out_quant)
             for _ in range(a.warmup):
-                graph.launch(gstream)
+                g.launch(gstream)
         torch.cuda.synchronize()
         gstart, gstop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         gstart.record(gstream)
         for _ in range(a.steps):
-            graph.launch(gstream)
+            g.launch(gstream)
         gstop.record(gstream)
         torch.cuda.synchronize()
         graph_ms = gstart.elapsed_time(gstop) / a.steps
-        graph.close()
-        del graph
+        g.close()
+        del g
     stage = {}
     for j in range(1, moe.NUM_STAGE_EVENTS):
         vals = [evs[i][j - 1].elapsed_time(evs[i][j]) for i in range(a.steps)]
         stage[moe.STAGES[j]] = sum(vals) / len(vals)
+    ids, _ = moe.moe_route(d["logits"], spec.top_k, spec.scoring, spec.renormalize)
+    touched = int(torch.unique(ids).numel())
     routed, shared = layer_flops(spec)
-    tflops = (routed + shared) / (ms * 1e-3) / 1e12
     dtype = "fp8" if spec.quant.startswith("fp8") else "bf16"
     g1_ms = stage["gemm1"]
     g1_tflops = gemm1_flops(spec) / (g1_ms * 1e-3) / 1e12
+    roof = layer_roofline(spec, touched)
+    res = {
+        "ms": ms, "wall": wall, "bm": bm, "stage": stage, "graph_ms": graph_ms,
+        "tflops": (routed + shared) / (ms * 1e-3) / 1e12, "dtype": dtype,
+        "g1_ms": g1_ms, "g1_tflops": g1_tflops, "layer_roofline": roof,
+        # GEMM-1's weights streamed once: the HBM floor of that kernel
+        "g1_hbm_floor_ms": touched * (2 if spec.activation in ("silu", "gelu") else 1) * spec.I
+        * spec.H * (1 if dtype == "fp8" else 2) / (PEAK_HBM_GBS * 1e9) * 1e3,
+    }
+    return res, d, (w, out, ws)
+
+
+def _roofline(spec, res, traffic):
+    dtype = res["dtype"]
+    return {"kernel": "routed GEMM-1 (gate+up, SiLU-mul fused)", "bound": "mfma",
+            "achieved": round(res["g1_tflops"], 2), "peak": PEAK_TFLOPS[dtype],
+            "unit": "TFLOP/s", "frac": round(res["g1_tflops"] / PEAK_TFLOPS[dtype], 4),
+            "traffic": traffic,
+            "timing": "GEMM-1's average duration over the K instrumented steps, from HIP "
+                      "events recorded on the launch stream before and after it inside "
+                      "moe_forward"}
+
+
+def main():
+    a = parse()
+    if a.write_traffic:
+        if a.copy_calibration <= 0:
+            raise SystemExit("--write-traffic needs --copy-calibration BYTES of the profiled run")
+        write_traffic(a)
+        return
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note, not implemented)"}))
+        sys.exit(2)
+    import torch
+    import mixture_experts_layer_routing_amd as moe
+
+    spec = find_spec(a.workload)
+    dev = "cuda"
+    res, d, keep = measure(a, torch, moe, spec, a.block_m, graph=not a.no_graph)
+    ms = res["ms"]
     traffic = None
     if os.path.exists(a.traffic):
         try:
@@ -343,6 +403,7 @@ def main():
                 traffic = rec.get("gemm1_bytes")
         except Exception:
             traffic = None
+    roof = res["layer_roofline"]
     line = {
         "metric": METRIC,
         "value": round(spec.T / (ms * 1e-3), 1),
@@ -354,29 +415,46 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": res["dtype"],
         "data": "synthetic (seeded; random-init weights of the stated shapes)",
         "config": {"workload": spec.name, "T": spec.T, "H": spec.H, "I": spec.I, "E": spec.E,
                    "top_k": spec.top_k, "scoring": spec.scoring, "renormalize": spec.renormalize,
-                   "quant": spec.quant, "shared_I": spec.shared_I, "block_m": bm,
+                   "quant": spec.quant, "shared_I": spec.shared_I, "block_m": res["bm"],
                    "parallelism": "none (1 GPU)"},
-        "tflops": round(tflops, 2),
-        "mfma_peak_frac": round(tflops / PEAK_TFLOPS[dtype], 4),
-        "stage_ms": {k: round(v, 4) for k, v in stage.items()},
-        "graph": None if graph_ms is None else {
-            "ms_per_step": round(graph_ms, 4), "tokens_per_s": round(spec.T / (graph_ms * 1e-3), 1)},
-        "wall_s": round(wall, 3),
-        "roofline": {"kernel": "routed GEMM-1 (gate+up, SiLU-mul fused)", "bound": "mfma",
-                     "achieved": round(g1_tflops, 2), "peak": PEAK_TFLOPS[dtype],
-                     "unit": "TFLOP/s", "frac": round(g1_tflops / PEAK_TFLOPS[dtype], 4),
-                     "traffic": traffic},
+        "tflops": round(res["tflops"], 2),
+        "mfma_peak_frac": round(res["tflops"] / PEAK_TFLOPS[res["dtype"]], 4),
+        "layer_roofline": dict(roof, frac=round(roof["ms"] / ms, 4)),
+        "stage_ms": {k: round(v, 4) for k, v in res["stage"].items()},
+        "graph": None if res["graph_ms"] is None else {
+            "ms_per_step": round(res["graph_ms"], 4),
+            "tokens_per_s": round(spec.T / (res["graph_ms"] * 1e-3), 1)},
+        "wall_s": round(res["wall"], 3),
+        "roofline": _roofline(spec, res, traffic),
     }
     cpu_inputs = None
     if not a.no_cpu_baseline:
         cpu_inputs = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in d.items()}
-    if not a.no_hbm_stages:
-        del d, w, out, ws
+    del d, keep
+    torch.cuda.empty_cache()
+    if a.fp8_leg != "none" and a.fp8_leg != spec.name:
+        # the fp8 path in the same run: its own roofline against the fp8 peak
+        # and GEMM-1's HBM floor, and the layer's fraction of its roofline
+        fspec = find_spec(a.fp8_leg)
+        fres, fd, fkeep = measure(a, torch, moe, fspec, 0, graph=False)
+        froof = fres["layer_roofline"]
+        line["fp8_leg"] = {
+            "workload": fspec.name, "ms_per_step": round(fres["ms"], 4),
+            "tokens_per_s": round(fspec.T / (fres["ms"] * 1e-3), 1),
+            "tflops": round(fres["tflops"], 2), "block_m": fres["bm"],
+            "stage_ms": {k: round(v, 4) for k, v in fres["stage"].items()},
+            "layer_roofline": dict(froof, frac=round(froof["ms"] / fres["ms"], 4)),
+            "roofline": dict(_roofline(fspec, fres, None),
+                             hbm_floor_ms=round(fres["g1_hbm_floor_ms"], 4),
+                             hbm_floor_frac=round(fres["g1_hbm_floor_ms"] / fres["g1_ms"], 4)),
+        }
+        del fd, fkeep
         torch.cuda.empty_cache()
+    if not a.no_hbm_stages:
         line.update(hbm_stages(torch, moe, dev))
     if a.copy_calibration:
         # the last GPU work of the run: the counter reduction takes the last
