@@ -263,8 +263,9 @@ def hbm_stages(torch, moe, dev):
         n = 1 << 24
         g = torch.Generator(device=dev)
         g.manual_seed(E)
-        idss = [torch.randint(0, E, (n // kk, kk), device=dev, dtype=torch.int32, generator=g)
-                for _ in range(4)]
+        # top-k routing: kk distinct experts per token, uniformly at random
+        idss = [torch.rand((n // kk, E), device=dev, generator=g).topk(kk, dim=1).indices
+                .to(torch.int32).contiguous() for _ in range(4)]
         ress = [moe.moe_align(ids, E, bm) for ids in idss]
 
         def al(i, idss=idss, ress=ress, E=E, bm=bm):

@@ -197,6 +197,16 @@ int moe_prepare(const uint16_t* a1, int T, int H, const float* topk_weights,
  * block cap = ceil(sorted cap / block_m).  workspace: moe_align_workspace_bytes.
  * Limits: block_m in {16, 32, 64, 128, 256}; 1 <= E <= 1024; ids in [0, E)
  * (precondition; out-of-range ids are dropped from every output).
+ * Paths: up to 32768 ids, one workgroup.  Above that, with E <= 256, at
+ * most 65536 ids per CU the stream may use and topk_ids 16-byte aligned,
+ * one launch that reads the ids once (not while the stream is capturing a
+ * graph, nor with the environment variable MOE_ALIGN_RESIDENT=0); otherwise
+ * three launches over tiles.  All paths give the same outputs.  The
+ * one-launch path needs its grid resident at once (one workgroup per CU)
+ * and waits on it for a bounded time: should a wait ever give up (another
+ * kernel holding CUs for about a second), num_tokens_post_padded is -1 and
+ * the other outputs are unspecified.  Calls that share a workspace must not
+ * overlap.
  */
 int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
               int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token_ids,
@@ -206,10 +216,12 @@ int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
 int moe_align_capacity(int T, int top_k, int E, int block_m,
                        int64_t* sorted_capacity, int64_t* block_capacity);
 /* (host) workspace moe_align needs: 0 for T*top_k <= 32768 ids; above that,
- * 4*E*(9*tiles + 1) bytes (per-expert counts of each eighth of a tile, the
- * tiles' per-expert totals and the expert totals), where tiles =
- * ceil(T*top_k / tile) and tile is the smallest power of two in
- * [2048, 8192] with tile*1024 >= T*top_k (8192 above 2^23 ids). */
+ * the larger of the tiled path's 4*E*(9*tiles + 1) bytes (per-expert counts
+ * of each eighth of a tile, the tiles' per-expert totals and the expert
+ * totals), where tiles = ceil(T*top_k / tile) and tile is the smallest power
+ * of two in [2048, 8192] with tile*1024 >= T*top_k (8192 above 2^23 ids),
+ * and the one-launch path's 8*257 + 4*256*E bytes (arrival flags and a go
+ * word, and up to 256 tiles' per-expert counts). */
 size_t moe_align_workspace_bytes(int T, int top_k, int E, int block_m);
 
 /*

@@ -185,6 +185,31 @@ def test_align_multi_tile_sizes(T, k, E, BM):
     _align_compare(ids, E, BM)
 
 
+@pytest.mark.parametrize("T,k,E,BM", [(20000, 8, 256, 128), (600000, 8, 64, 64),
+                                      (300000, 1, 3, 16), (4097, 8, 256, 64)])
+def test_align_tiled_path_where_the_resident_one_applies(T, k, E, BM, monkeypatch):
+    """The three-launch tiled path, forced (MOE_ALIGN_RESIDENT=0) on sizes
+    the one-launch resident path takes by default: both are bit-exact."""
+    _announce(f"align tiled T={T} k={k} E={E} BM={BM}")
+    monkeypatch.setenv("MOE_ALIGN_RESIDENT", "0")
+    g = torch.Generator().manual_seed(T + E + 1)
+    ids = torch.randint(0, E, (T, k), generator=g, dtype=torch.int32)
+    _align_compare(ids, E, BM)
+
+
+@pytest.mark.parametrize("n,E,BM", [(1 << 24, 256, 128), (1 << 24, 8, 256),
+                                    ((1 << 24) - 1000, 16, 32), (204 * 1024 + 77, 256, 16),
+                                    (3 * 65536 + 5, 9, 64)])
+def test_align_resident_grid_shapes(n, E, BM):
+    """The resident path at its capacity (2^24 ids: 256 workgroups of 65536
+    ids, 64 per lane) and below it: a ragged last tile, a grid that is not a
+    multiple of the 8 XCDs, the ballot rank (E <= 8) and the table rank."""
+    _announce(f"align resident n={n} E={E} BM={BM}")
+    g = torch.Generator().manual_seed(n % 9973 + E)
+    ids = torch.randint(0, E, (n, 1), generator=g, dtype=torch.int32)
+    _align_compare(ids, E, BM)
+
+
 def test_align_is_deterministic_across_runs():
     moe = _moe()
     g = torch.Generator().manual_seed(3)
