@@ -220,8 +220,9 @@ int moe_align_capacity(int T, int top_k, int E, int block_m,
  * of each eighth of a tile, the tiles' per-expert totals and the expert
  * totals), where tiles = ceil(T*top_k / tile) and tile is the smallest power
  * of two in [2048, 8192] with tile*1024 >= T*top_k (8192 above 2^23 ids),
- * and the one-launch path's 8*257 + 4*256*E bytes (arrival flags and a go
- * word, and up to 256 tiles' per-expert counts). */
+ * and the one-launch path's 8*257 + 4*G*E bytes with G = min(256,
+ * ceil(T*top_k / 4096)) (arrival flags and a go word; up to G tiles'
+ * per-expert counts). */
 size_t moe_align_workspace_bytes(int T, int top_k, int E, int block_m);
 
 /*

@@ -622,6 +622,50 @@ __device__ __forceinline__ uint32_t rank_rows(const int32_t* __restrict__ wids, 
   return transposed;
 }
 
+// Grid barrier over resident workgroups, in two halves.  arrive: thread 0
+// publishes (release) flag[g] = epoch after the workgroup's stores (the
+// caller synchronises the workgroup first).  await: workgroup 0 waits for
+// every flag, then raises go = epoch; the others wait for go.  Afterwards
+// each workgroup's loads see what every workgroup stored before arriving.
+// The waits give up after kMaxSpins polls; await then returns false in
+// every thread of the workgroup.
+__device__ __forceinline__ void grid_arrive(uint64_t* flag, uint64_t epoch, int g) {
+  if (threadIdx.x == 0) __hip_atomic_store(flag + g, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ bool grid_await(uint64_t* flag, uint64_t* go, uint64_t epoch, int g, int G, int* okf) {
+  const int tid = threadIdx.x;
+  if (g == 0) {
+    int ok = 1;
+    if (tid < G) {
+      uint32_t spins = 0;
+      while (__hip_atomic_load(flag + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins == kMaxSpins) { ok = 0; break; }
+      }
+    }
+    ok = __syncthreads_and(ok);
+    if (tid == 0) {
+      *okf = ok;
+      if (ok) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(go, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  } else if (tid == 0) {
+    int ok = 1;
+    uint32_t spins = 0;
+    while (__hip_atomic_load(go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins == kMaxSpins) { ok = 0; break; }
+    }
+    *okf = ok;
+  }
+  if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
+  return *okf != 0;
+}
+
 // Workgroup g owns the ids [g*tile, (g+1)*tile), tile = 4096*rows: wave w
 // owns 256*rows consecutive ids and reads them as rows of 256 (16 B a lane),
 // each row transposed through LDS so that lane l ranks ids 64j + l of it
@@ -651,7 +695,10 @@ __global__ __launch_bounds__(kResThreads) void align_resident_kernel(
   // the wave index as a scalar: the wave's pointers stay in scalar registers
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = gridDim.x, g = blockIdx.x;
+  // tile g: the tiles are dealt to the XCDs in contiguous ranges, so that
+  // the line where one tile's run of an expert meets the next tile's is
+  // written in one L2
+  const int G = gridDim.x, g = xcd_tile(blockIdx.x, G);
   constexpr int tile = kResThreads * 4 * ROWS;
   const int t0 = g * tile;
   const int lbase = wave * 256 * ROWS;   // the wave's first id, local to the tile
@@ -685,10 +732,8 @@ __global__ __launch_bounds__(kResThreads) void align_resident_kernel(
   }
   __syncthreads();
   const int tile_total = block_exclusive_scan<kResThreads>(lb, E, partial);
-  if (tid == 0) {
-    lb[E] = tile_total;
-    __hip_atomic_store(flags + g, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid == 0) lb[E] = tile_total;
+  grid_arrive(flags, epoch, g);
   for (int e = tid; e < E; e += kResThreads)
     for (int w = 0; w < kResWaves; ++w) cur[w * kResMaxE + e] += lb[e];
   __syncthreads();
@@ -718,40 +763,12 @@ __global__ __launch_bounds__(kResThreads) void align_resident_kernel(
           static_cast<uint16_t>(lbase + 256 * r + (tr ? 64 * q + lane : 4 * lane + q));
     }
   }
-  // ---- barrier: workgroup 0 collects the flags and raises go -------------
-  if (g == 0) {
-    int ok = 1;
-    if (tid < G) {
-      uint32_t spins = 0;
-      while (__hip_atomic_load(flags + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins == kMaxSpins) { ok = 0; break; }
-      }
-    }
-    ok = __syncthreads_and(ok);
-    if (tid == 0) {
-      *okf = ok;
-      if (ok) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __hip_atomic_store(go, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  } else if (tid == 0) {
-    int ok = 1;
-    uint32_t spins = 0;
-    while (__hip_atomic_load(go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins == kMaxSpins) { ok = 0; break; }
-    }
-    *okf = ok;
-  }
-  if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  __syncthreads();
-  if (!*okf) {
+  // ---- barrier: every tile's counts are published ------------------------
+  if (!grid_await(flags, go, epoch, g, G, okf)) {
     if (tid == 0) __hip_atomic_store(ntp, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  // ---- expert totals and the earlier tiles' counts, from the count rows --
+  // ---- expert totals tt and the earlier tiles' counts gpre, from the rows --
   for (int e = tid; e < E; e += kResThreads) { tt[e] = 0; gpre[e] = 0; }
   __syncthreads();
   {
@@ -864,8 +881,15 @@ int resident_grid_capacity(hipStream_t s) {
   return std::min(cus, kResMaxGrid);
 }
 
-size_t resident_workspace_bytes(int E) {
-  return (kResMaxGrid + 1) * sizeof(uint64_t) + static_cast<size_t>(kResMaxGrid) * E * sizeof(int32_t);
+// A bound on the resident grid for n ids: a tile holds at least 4096 ids.
+int64_t resident_grid_bound(int64_t n) {
+  return std::min<int64_t>(kResMaxGrid, (n + kResThreads * 4 - 1) / (kResThreads * 4));
+}
+
+// the arrival flags and the go word; the count rows [G][E]
+size_t resident_workspace_bytes(int64_t n, int E) {
+  return (kResMaxGrid + 1) * sizeof(uint64_t) +
+         static_cast<size_t>(resident_grid_bound(n)) * E * sizeof(int32_t);
 }
 
 // A new epoch per call: flags and the go word from earlier calls (or from
@@ -931,7 +955,7 @@ size_t align_workspace_bytes(int64_t n, int E) {
   const AlignPlan p = plan(n, E);
   if (p.ntiles == 0) return 0;
   const size_t tiled = (static_cast<size_t>(p.ntiles) * (kTileWaves + 1) + 1) * E * sizeof(int32_t);
-  return std::max(tiled, resident_workspace_bytes(E));
+  return std::max(tiled, resident_workspace_bytes(n, E));
 }
 
 void launch_align(const int32_t* ids, int64_t n, int E, int BM, int32_t* counts,

@@ -75,9 +75,9 @@ def test_align_workspace_is_zero_for_one_tile(moe):
     # 2^20 ids: 512 tiles of 2048; 2^22: 1024 of 4096
     assert lib.moe_align_workspace_bytes(1 << 17, 8, 64, 64) == (512 * 9 + 1) * 64 * 4
     assert lib.moe_align_workspace_bytes(1 << 21, 2, 8, 256) == (1024 * 9 + 1) * 8 * 4
-    # 40000 ids: 20 tiles of 2048 need less than the one-launch path's 257
-    # 64-bit flags and 256 tiles' expert counts
-    assert lib.moe_align_workspace_bytes(5000, 8, 256, 16) == 8 * 257 + 4 * 256 * 256
+    # 40000 ids, E=2: 20 tiles of 2048 need less than the one-launch path's
+    # 257 64-bit flags and the expert counts of up to 10 tiles of 4096
+    assert lib.moe_align_workspace_bytes(20000, 2, 2, 16) == 8 * 257 + 4 * 10 * 2
 
 
 def _bad(moe, fn, *args):
