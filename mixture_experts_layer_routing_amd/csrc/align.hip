@@ -54,6 +54,7 @@
 // run-to-run identical.
 #include "moe_device.h"
 #include "launch.h"
+#include "route_device.h"
 
 #include <algorithm>
 #include <atomic>
@@ -835,6 +836,100 @@ __global__ __launch_bounds__(kResThreads) void align_resident_kernel(
                  sorted);
 }
 
+// ---- decode prologue: routing and align in one wave (T*top_k <= 64) ------
+// Decode-sized batches spend more time launching the routing and align
+// kernels than computing them; this one wave does both.  Lane l of the wave
+// then holds flat row l's expert: one peer mask per lane gives the counts
+// (its leader's popcount) and the stable slots (peers below); the padded
+// offsets are a wave scan over the experts; pad slots and the tail get the
+// sentinel from loops over the touched experts (at most 64) and the tail.
+// The wave's LDS operations complete in issue order, so no barrier is
+// needed between its LDS writes and reads.
+constexpr int kPrologueMaxIds = 64;
+constexpr int kPrologueMaxE = 1024;
+
+template <int VPL>
+__global__ __launch_bounds__(64) void decode_prologue_kernel(
+    const float* __restrict__ logits, int T, int E, int top_k, int scoring, int renorm,
+    int32_t* __restrict__ ids, float* __restrict__ weights, int nbits, int BM,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+    int64_t sorted_cap, int32_t* __restrict__ block_ids, int64_t block_cap,
+    int32_t* __restrict__ ntp) {
+  __shared__ int flat[kPrologueMaxIds];
+  __shared__ int cnt[kPrologueMaxE];
+  __shared__ int off[kPrologueMaxE + 1];
+  const int lane = threadIdx.x;
+  const int n = T * top_k;
+  for (int t = 0; t < T; ++t) {
+    int e;
+    float w;
+    route_token<VPL>(logits + static_cast<size_t>(t) * E, E, top_k, scoring, renorm, &e, &w);
+    if (lane < top_k) {
+      ids[t * top_k + lane] = e;
+      weights[t * top_k + lane] = w;
+      flat[t * top_k + lane] = e;
+    }
+  }
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  const int key = lane < n ? flat[lane] : -1;
+  const bool valid = static_cast<unsigned>(key) < static_cast<unsigned>(E);
+  const uint64_t m = peer_mask(key, valid, nbits);
+  const uint64_t below = lanemask_lt();
+  const bool leader = valid && (m & below) == 0;
+  if (leader) cnt[key] = __builtin_popcountll(m);
+  // padded offsets: lane l scans experts [l*per, (l+1)*per)
+  const int per = (E + 63) / 64;
+  const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) local += (cnt[e] + BM - 1) / BM * BM;
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int up = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += up;
+  }
+  int run = incl - local;
+  for (int e = e0; e < e1; ++e) {
+    const int c = cnt[e];
+    off[e] = run;
+    counts[e] = c;
+    offsets[e] = run;
+    run += (c + BM - 1) / BM * BM;
+  }
+  const int total = __shfl(incl, 63, 64);
+  if (lane == 0) {
+    off[E] = total;
+    offsets[E] = total;
+    ntp[0] = total;
+  }
+  // stable slots: the peers below, after the expert's offset
+  if (valid) sorted[off[key] + __builtin_popcountll(m & below)] = lane;
+  // the sentinel in each touched expert's pad slots, one expert at a time
+  uint64_t lead = __ballot(leader);
+  while (lead) {
+    const int src = __builtin_ctzll(lead);
+    lead &= lead - 1;
+    const int e = __shfl(key, src, 64);
+    const int c = __shfl(cnt[key > 0 ? key : 0], src, 64);
+    for (int p = off[e] + c + lane; p < off[e + 1]; p += 64) sorted[p] = n;
+  }
+  for (int64_t p = total + lane; p < sorted_cap; p += 64) sorted[p] = n;
+  for (int64_t b = lane; b < block_cap; b += 64) {
+    int owner = -1;
+    if (b * BM < total) {
+      const int row = static_cast<int>(b) * BM;
+      int lo = 0, hi = E - 1;   // the last expert whose offset is <= row
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= row) lo = mid;
+        else hi = mid - 1;
+      }
+      owner = lo;
+    }
+    block_ids[b] = owner;
+  }
+}
+
 struct AlignPlan {
   int tile_ids, ntiles;
 };
@@ -986,6 +1081,28 @@ void launch_align(const int32_t* ids, int64_t n, int E, int BM, int32_t* counts,
     align_scatter_kernel<kMaxE><<<p.ntiles, kTileThreads, 0, s>>>(
         ids, nn, E, nbits, BM, p.tile_ids, p.ntiles, sub, tcol, tot, counts, offsets, ntp,
         block_ids, block_cap, sorted, sorted_cap);
+}
+
+bool decode_prologue_fits(int T, int top_k, int E, int64_t sorted_cap) {
+  return static_cast<int64_t>(T) * top_k <= kPrologueMaxIds && E <= kPrologueMaxE &&
+         sorted_cap <= 16384;
+}
+
+void launch_decode_prologue(const float* logits, int T, int E, int top_k, int scoring,
+                            int renorm, int32_t* ids, float* weights, int BM, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted, int64_t sorted_cap,
+                            int32_t* block_ids, int64_t block_cap, int32_t* ntp, hipStream_t s) {
+  const int nbits = ceil_log2(E);
+  auto go = [&](auto vpl) {
+    decode_prologue_kernel<decltype(vpl)::value><<<1, 64, 0, s>>>(
+        logits, T, E, top_k, scoring, renorm, ids, weights, nbits, BM, counts, offsets, sorted,
+        sorted_cap, block_ids, block_cap, ntp);
+  };
+  if (E <= 64) go(std::integral_constant<int, 1>{});
+  else if (E <= 128) go(std::integral_constant<int, 2>{});
+  else if (E <= 256) go(std::integral_constant<int, 4>{});
+  else if (E <= 512) go(std::integral_constant<int, 8>{});
+  else go(std::integral_constant<int, 16>{});
 }
 
 }  // namespace moe

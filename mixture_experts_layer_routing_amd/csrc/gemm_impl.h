@@ -833,7 +833,8 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
             const int r = row_w + fm * MF + acc_row<MF>(v, lane);
             if (r < row_end) {
               const int cc = wn * WN + fn * MF + acc_col<MF>(lane);
-              part[static_cast<int64_t>(m0 + r) * p.ldp + g * p.inter + n0 + cc] =
+              const int prow = p.part_flat ? p.sorted[m0 + r] : m0 + r;
+              part[static_cast<int64_t>(prow) * p.ldp + g * p.inter + n0 + cc] =
                   acc[g][fm][fn][v];
             }
           }

@@ -15,6 +15,14 @@ void launch_prepare(const uint16_t* a1, int T, int H, const float* w, int apply_
                     int quant, void* a1q, float* a1q_scale, hipStream_t s);
 
 size_t align_workspace_bytes(int64_t n, int E);
+// Routing and align of a decode-sized batch in one launch (one wave), with
+// the outputs of launch_route and launch_align; only where
+// decode_prologue_fits (T*top_k <= 64, E <= 1024, sorted capacity <= 16384).
+bool decode_prologue_fits(int T, int top_k, int E, int64_t sorted_cap);
+void launch_decode_prologue(const float* logits, int T, int E, int top_k, int scoring,
+                            int renorm, int32_t* ids, float* weights, int BM, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted, int64_t sorted_cap,
+                            int32_t* block_ids, int64_t block_cap, int32_t* ntp, hipStream_t s);
 void launch_align(const int32_t* ids, int64_t n, int E, int BM, int32_t* counts,
                   int32_t* offsets, int32_t* sorted, int64_t sorted_cap, int32_t* block_ids,
                   int64_t block_cap, int32_t* ntp, void* ws, hipStream_t s);
@@ -24,10 +32,14 @@ void launch_align(const int32_t* ids, int64_t n, int E, int BM, int32_t* counts,
 void launch_batched_schedule(const int32_t* counts, int E, int M, int bm, int64_t block_cap,
                              int32_t* sorted, int32_t* block_expert, int32_t* ntp, hipStream_t s);
 
+// ypart / shpart (optional, only without gamma): split-K partials of the
+// routed rows [ysplit][T*k][H] and of the shared expert [shsplit][T][H],
+// summed here in split order and rounded to bf16 in place of y / sh.
 void launch_finalize(void* out, float* out_scale, int out_quant, const uint16_t* y,
                      const float* w, int T, int k, int H, int woi, const uint16_t* sh,
                      const uint16_t* res, uint16_t* res_out, const uint16_t* gamma, float eps,
-                     hipStream_t s);
+                     hipStream_t s, const float* ypart = nullptr, int ysplit = 1,
+                     const float* shpart = nullptr, int shsplit = 1);
 
 // One grouped-GEMM launch (see gemm_impl.h).
 struct GemmParams {
@@ -62,6 +74,10 @@ struct GemmParams {
   float* partial;
   int64_t part_rows;
   int ldp;
+  // Routed second GEMM only: index the partial rows by the flat row
+  // t*top_k + j (sorted[row]) instead of the sorted row, pad rows skipped,
+  // so that finalize can sum a token's partials itself.
+  int part_flat;
   // Weight rows through a 3-deep ring where a tile exists for it
   // (GemmCfg::SPLIT): set for the routed bf16 GEMMs, whose 256-row tiles
   // stream weights with little reuse at medium T.

@@ -328,11 +328,22 @@ int tiles_exist(int T, int H, const moe_weights* w, int activation, int bm) {
   return MOE_OK;
 }
 
+// Second-GEMM partials left to finalize (whole-layer forward only): when a
+// second GEMM splits its K and the region is given, the GEMM writes its
+// partials there and the split-K reduction launch is skipped; ysplit /
+// shsplit report the split (1: fused_expert_output / shared_out written).
+struct Deferred {
+  float* ypart;    // [s2][T*top_k][H]
+  float* shpart;   // [s4][T][H]
+  int ysplit = 1, shsplit = 1;
+};
+
 int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
                 const float* shared_in_scale, const Routed& rt, int T, int H, const moe_weights* w,
                 int activation, const int32_t* sorted, const int32_t* block_expert,
                 const int32_t* ntp, const int32_t* offsets, int bm, uint16_t* feo,
-                uint16_t* shared_out, void* ws, const StageEvents& se, hipStream_t s) {
+                uint16_t* shared_out, void* ws, const StageEvents& se, hipStream_t s,
+                Deferred* defer = nullptr) {
   using namespace moe;
   const bool fp8 = quant_fp8(w->quant);
   const bool gated = act_gated(activation);
@@ -421,8 +432,15 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   q.out = feo;
   q.ldo = H;
   split(q, sp.s2, rows, H);
+  const bool defer_y = defer && defer->ypart && sp.s2 > 1;
+  if (defer_y) {
+    q.partial = defer->ypart;
+    q.part_rows = nflat;
+    q.part_flat = 1;
+    defer->ysplit = sp.s2;
+  }
   launch(GEMM_Y_ROUTED, bm2, bn2, q, cp.block_cap * (bm / bm2));
-  if (sp.s2 > 1)
+  if (sp.s2 > 1 && !defer_y)
     launch_splitk_y(part, sp.s2, rows, H, rows, ntp, sorted, nflat, rt.T, H, feo, H, s);
   se.mark(5);
   if (w->shared_inter > 0) {
@@ -466,8 +484,13 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
     e.out = shared_out;
     e.ldo = H;
     split(e, sp.s4, T, H);
+    const bool defer_sh = defer && defer->shpart && sp.s4 > 1;
+    if (defer_sh) {
+      e.partial = defer->shpart;
+      defer->shsplit = sp.s4;
+    }
     launch(GEMM_Y_DENSE, dbm4, bn4, e, mblk4);
-    if (sp.s4 > 1)
+    if (sp.s4 > 1 && !defer_sh)
       launch_splitk_y(part, sp.s4, T, H, T, nullptr, nullptr, 0, T, H, shared_out, H, s);
   }
   se.mark(6);
@@ -786,6 +809,8 @@ struct ForwardLayout {
   size_t experts_ws_bytes;
   uint16_t* feo;
   uint16_t* shared_out;
+  float* ypart;    // split second GEMMs' partials, summed by finalize (or null)
+  float* shpart;
 };
 
 size_t forward_layout(int T, int H, int top_k, const moe_weights* w, int activation, int bm,
@@ -821,6 +846,11 @@ size_t forward_layout(int T, int H, int top_k, const moe_weights* w, int activat
   L->feo = static_cast<uint16_t*>(c.take(static_cast<size_t>(n) * H * 2));
   L->shared_out = w->shared_inter > 0 ? static_cast<uint16_t*>(c.take(static_cast<size_t>(T) * H * 2))
                                       : nullptr;
+  const SplitPlan sp = split_plan(standard_rows(T, top_k, E, bm), T, H, w, activation, bm);
+  L->ypart = sp.s2 > 1 ? static_cast<float*>(c.take(static_cast<size_t>(sp.s2) * n * H * 4)) : nullptr;
+  L->shpart = (w->shared_inter > 0 && sp.s4 > 1)
+                  ? static_cast<float*>(c.take(static_cast<size_t>(sp.s4) * T * H * 4))
+                  : nullptr;
   return c.used;
 }
 
@@ -892,8 +922,16 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
   const int64_t n = static_cast<int64_t>(T) * top_k;
   const Caps cp = capacities(T, top_k, E, bm);
 
+  // decode-sized batches: routing and align in one launch (stage 1 then
+  // covers both, and the align stage is empty)
+  const bool prologue = moe::decode_prologue_fits(T, top_k, E, cp.sorted_cap);
   se.mark(0);
-  moe::launch_route(logits, T, E, top_k, scoring, renormalize ? 1 : 0, L.ids, L.tw, stream);
+  if (prologue)
+    moe::launch_decode_prologue(logits, T, E, top_k, scoring, renormalize ? 1 : 0, L.ids, L.tw, bm,
+                                L.counts, L.offsets, L.sorted, cp.sorted_cap, L.blocks,
+                                cp.block_cap, L.ntp, stream);
+  else
+    moe::launch_route(logits, T, E, top_k, scoring, renormalize ? 1 : 0, L.ids, L.tw, stream);
   se.mark(1);
   const void* a1q = x;
   if (quant_fp8(quant) || apply_router_weight_on_input) {
@@ -915,16 +953,21 @@ int moe_forward(const uint16_t* x, const float* logits, int T, int H, int top_k,
     }
   }
   se.mark(2);
-  moe::launch_align(L.ids, n, E, bm, L.counts, L.offsets, L.sorted, cp.sorted_cap, L.blocks,
-                    cp.block_cap, L.ntp, L.align_ws, stream);
+  if (!prologue)
+    moe::launch_align(L.ids, n, E, bm, L.counts, L.offsets, L.sorted, cp.sorted_cap, L.blocks,
+                      cp.block_cap, L.ntp, L.align_ws, stream);
   se.mark(3);
+  // (with RMSNorm finalize needs whole rows in one workgroup, too few at
+  // decode sizes to read split partials quickly: reduce the splits first)
+  Deferred df{gamma ? nullptr : L.ypart, gamma ? nullptr : L.shpart};
   int st = run_experts(a1q, L.a1q_scale, shin, shin_scale, standard_rows(T, top_k, E, bm), T, H,
                        weights, activation, L.sorted, L.blocks, L.ntp, L.offsets, bm, L.feo,
-                       L.shared_out, L.experts_ws, se, stream);
+                       L.shared_out, L.experts_ws, se, stream, &df);
   if (st) return st;
   moe::launch_finalize(output, output_scale, out_quant, L.feo, L.tw, T, top_k, H,
                        apply_router_weight_on_input ? 1 : 0, L.shared_out, residual, residual_out,
-                       gamma, eps, stream);
+                       gamma, eps, stream, df.ysplit > 1 ? L.ypart : nullptr, df.ysplit,
+                       df.shsplit > 1 ? L.shpart : nullptr, df.shsplit);
   se.mark(7);
   return check_launch("moe_forward");
 }

@@ -2,6 +2,7 @@
 the CPU oracle: reduced cases element by element, the five workload families
 at their full sizes on sampled tokens (route and align checked in full)."""
 
+import dataclasses
 import gc
 import sys
 
@@ -230,6 +231,48 @@ def test_forward_reduced(spec):
                         _ref_f64(spec, refs["mirrored"]), _path(spec), f"{spec.name} BM={bm}",
                         min_identical=0.9 if _path(spec) == "bf16" else None,
                         allowance=allowance, maxnorm_slack=slack)
+
+
+@pytest.mark.parametrize("name,extra", [
+    ("decode_split_mini", {}), ("decode_split_fp8_mini", {}), ("decode_split_no_mul_mini", {}),
+    ("decode_split_mini", {"residual": True, "out_quant": "fp8"}),
+    ("decode_split_fp8_mini", {"residual": True, "rmsnorm": True}),
+    ("fp8_out_mini", {}), ("llama4_mini", {}), ("finalize_fused_mini", {})],
+    ids=lambda v: v if isinstance(v, str) else "+".join(v) or "plain")
+def test_forward_equals_the_staged_calls(name, extra):
+    """moe_forward is, bit for bit, the composition of the staged calls:
+    route -> prepare -> align -> experts -> finalize.  That holds where a
+    second GEMM splits K too: the forward leaves those fp32 partials to
+    finalize, which sums them in split order and rounds to bf16 before the
+    weighting, as the standalone split-K reduction does for moe_experts.
+    The decode cases split both the routed and the shared second GEMM."""
+    spec = dataclasses.replace(next(s for s in PARITY_CASES if s.name == name), **extra)
+    _announce(f"forward vs staged {name} {extra}")
+    moe = _moe()
+    dd = {k: v.to(DEV) for k, v in make_layer_inputs(spec).items()}
+    w = _weights(moe, dd, spec.quant)
+    T, E, k = spec.T, spec.E, spec.top_k
+    woi = spec.apply_router_weight_on_input
+    bm = moe.moe_pick_block_m(T, k, E, spec.quant)
+    out_f, scale_f, _ = moe.moe_forward(dd["x"], dd["logits"], w, k, spec.scoring, spec.renormalize,
+                                        woi, spec.activation, bm, dd.get("residual"),
+                                        dd.get("gamma"), spec.eps, spec.out_quant)
+    ids, tw = moe.moe_route(dd["logits"], k, spec.scoring, spec.renormalize)
+    a1q, a1s = moe.moe_prepare(dd["x"], tw, ids, woi, quant=spec.quant)
+    shin, shin_s = a1q, a1s
+    if "shared_w13" in dd and woi:
+        # the shared expert reads the unweighted input
+        shin, shin_s = moe.moe_prepare(dd["x"], None, ids, False, quant=spec.quant)
+    al = moe.moe_align(ids, E, bm)
+    feo, sho = moe.moe_experts(a1q, a1s, w, k, al, bm, spec.activation, shared_in=shin,
+                               shared_in_scale=shin_s)
+    out_s, scale_s, _ = moe.moe_finalize(feo, tw, ids, woi, shared=sho, residual=dd.get("residual"),
+                                         gamma=dd.get("gamma"), eps=spec.eps,
+                                         out_quant=spec.out_quant)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_numpy_bits(out_f), to_numpy_bits(out_s))
+    if scale_f is not None:
+        np.testing.assert_array_equal(scale_f.cpu().numpy(), scale_s.cpu().numpy())
 
 
 def _allowance(spec, ref, d, hw):
