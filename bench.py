@@ -60,8 +60,10 @@ def parse():
     return ap.parse_args()
 
 
-# Routed GEMM-1: the grouped GEMM instantiated with A_GATHER (0) and EPI_Z (0).
+# Routed GEMM-1: the grouped GEMM instantiated with A_GATHER (0) and EPI_Z (0);
+# routed GEMM-2: A_ROWS (1) and EPI_OUT_ROUTED (1).
 GEMM1_KERNEL_RE = r"grouped_gemm_kernel<.*GemmCfg<(-?\d+, ){5}(true|false), (true|false), 0, 0,"
+GEMM2_KERNEL_RE = r"grouped_gemm_kernel<.*GemmCfg<(-?\d+, ){5}(true|false), (true|false), 1, 1,"
 COPY_KERNEL_RE = r"elementwise|vectorized"
 
 
@@ -83,8 +85,9 @@ def kernel_sources_digest():
     return h.hexdigest()
 
 
-def _pmc_means(run_dir, counter):
-    """Per-dispatch mean of one counter for the GEMM-1 and copy kernels."""
+def _pmc_means(run_dir, counter, kernel_re=GEMM1_KERNEL_RE):
+    """Per-dispatch mean of one counter for one GEMM's kernels and the copy
+    kernel."""
     import csv
     import glob
     import re
@@ -97,7 +100,7 @@ def _pmc_means(run_dir, counter):
             if r["Counter_Name"] != counter:
                 continue
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
-            if re.search(GEMM1_KERNEL_RE, name):
+            if re.search(kernel_re, name):
                 gemm1.append(v)
             elif re.search(COPY_KERNEL_RE, name):
                 copies.append((int(r["Dispatch_Id"]), v))
@@ -113,6 +116,8 @@ def write_traffic(a):
     rec = {"kernel": "routed GEMM-1", "kernel_regex": GEMM1_KERNEL_RE,
            "sources_sha256": kernel_sources_digest()}
     total = 0.0
+    g2 = {"kernel": "routed GEMM-2", "kernel_regex": GEMM2_KERNEL_RE}
+    total2 = 0.0
     for counter, run_dir in (("FETCH_SIZE", a.write_traffic[0]), ("WRITE_SIZE", a.write_traffic[1])):
         g_kib, c_kib, n = _pmc_means(run_dir, counter)
         factor = c_kib * 1024.0 / a.copy_calibration     # counter bytes per true byte
@@ -121,7 +126,13 @@ def write_traffic(a):
                         "copy_true_bytes": a.copy_calibration, "factor": round(factor, 4),
                         "gemm1_bytes": round(g_kib * 1024.0 / factor)}
         total += g_kib * 1024.0 / factor
+        g2_kib, _, _ = _pmc_means(run_dir, counter, GEMM2_KERNEL_RE)
+        g2[counter] = {"kib_per_dispatch": round(g2_kib, 1), "factor": round(factor, 4),
+                       "bytes": round(g2_kib * 1024.0 / factor)}
+        total2 += g2_kib * 1024.0 / factor
     rec["gemm1_bytes"] = round(total)
+    g2["bytes"] = round(total2)
+    rec["gemm2"] = g2
     tr = {}
     if os.path.exists(a.traffic):
         tr = json.load(open(a.traffic))
@@ -367,6 +378,18 @@ def measure(a, torch, moe, spec, block_m=0, graph=True):
     return res, d, (w, out, ws)
 
 
+def gemm1_traffic(a, spec):
+    """GEMM-1's HBM bytes per launch from the counter record of this
+    workload, or None when there is none or it was taken on other GEMM code."""
+    if not os.path.exists(a.traffic):
+        return None
+    try:
+        rec = json.load(open(a.traffic)).get(spec.name, {})
+    except Exception:
+        return None
+    return rec.get("gemm1_bytes") if rec.get("sources_sha256") == kernel_sources_digest() else None
+
+
 def _roofline(spec, res, traffic):
     dtype = res["dtype"]
     return {"kernel": "routed GEMM-1 (gate+up, SiLU-mul fused)", "bound": "mfma",
@@ -396,14 +419,7 @@ def main():
     dev = "cuda"
     res, d, keep = measure(a, torch, moe, spec, a.block_m, graph=not a.no_graph)
     ms = res["ms"]
-    traffic = None
-    if os.path.exists(a.traffic):
-        try:
-            rec = json.load(open(a.traffic)).get(spec.name, {})
-            if rec.get("sources_sha256") == kernel_sources_digest():
-                traffic = rec.get("gemm1_bytes")
-        except Exception:
-            traffic = None
+    traffic = gemm1_traffic(a, spec)
     roof = res["layer_roofline"]
     line = {
         "metric": METRIC,
@@ -449,7 +465,7 @@ def main():
             "tflops": round(fres["tflops"], 2), "block_m": fres["bm"],
             "stage_ms": {k: round(v, 4) for k, v in fres["stage"].items()},
             "layer_roofline": dict(froof, frac=round(froof["ms"] / fres["ms"], 4)),
-            "roofline": dict(_roofline(fspec, fres, None),
+            "roofline": dict(_roofline(fspec, fres, gemm1_traffic(a, fspec)),
                              hbm_floor_ms=round(fres["g1_hbm_floor_ms"], 4),
                              hbm_floor_frac=round(fres["g1_hbm_floor_ms"] / fres["g1_ms"], 4)),
         }
