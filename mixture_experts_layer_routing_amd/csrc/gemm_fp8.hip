@@ -11,12 +11,6 @@
 
 namespace moe {
 
-// Split rings (GemmCfg::SPLIT) for the 128-row first-GEMM and 256-row
-// tiles: measured on MI355X at DeepSeek-V3 T=8192 the first GEMM did not
-// change (3.55 ms either way: its loads are bound by L2->LDS throughput,
-// not by latency) and the second GEMM lost 7 %, so they are off.
-constexpr bool kFp8Split = false;
-
 // Each dispatcher launches the tile for (block_m, width) and returns 0, or
 // returns -1 without launching when no such tile exists.  With p == nullptr
 // it only answers whether the tile exists (the host asks before it
@@ -27,39 +21,32 @@ static int run(const GemmParams* p, int64_t max_mblk, hipStream_t s) {
   return 0;
 }
 
-// Tiles whose weight rows stream through a 3-deep ring (GemmCfg::SPLIT):
-// the split layout needs the tile's whole activation-scale table in LDS, so
-// a launch whose k-tiles exceed its capacity runs the two-stage tile Legacy.
-template <class Split, class Legacy>
-static int run_split(const GemmParams* p, int64_t max_mblk, hipStream_t s) {
-  if (p && p->K / 128 / p->ksplit > GemmLds<Split>::SA_KB) return run<Legacy>(p, max_mblk, s);
-  return run<Split>(p, max_mblk, s);
-}
+// LDS stages: three for the 128-row first-GEMM tiles (two k-tiles of loads
+// in flight, 144 KB; the activation scales then come by a direct load per
+// k-tile into a ring unless the tile's whole table fits beside), two for the
+// rest (a third stage made the 256-row second GEMM slower: DeepSeek-V3
+// T=8192 2.03 -> 2.15 ms).
+constexpr int fp8_stages(int bm, int ep) { return bm == 128 && ep == EPI_Z ? 3 : 2; }
 
+// First GEMMs below 256 rows run with swapped operands (GemmCfg::SWAP).
 template <int BM, int BNZ, int WM, int WN, int MF, bool GATED, int AM, int EP>
-using Fp8Cfg = GemmCfg<BM, BNZ, WM, WN, MF, true, GATED, AM, EP>;
-template <int BM, int BNZ, int WM, int WN, int MF, bool GATED, int AM, int EP>
-using Fp8Split = GemmCfg<BM, BNZ, WM, WN, MF, true, GATED, AM, EP, 2, 128, kFp8Split>;
+using Fp8Cfg = GemmCfg<BM, BNZ, WM, WN, MF, true, GATED, AM, EP, fp8_stages(BM, EP), 128, false,
+                       EP == EPI_Z && BM < 256>;
 
 template <int AM, int EP, bool GATED>
 static int dispatch_bm(int block_m, const GemmParams* p, int64_t max_mblk, hipStream_t s) {
   switch (block_m) {
-    case 16: return run<GemmCfg<16, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s);
-    case 32: return run<GemmCfg<32, 128, 1, 4, 16, true, GATED, AM, EP>>(p, max_mblk, s);
-    case 64: return run<GemmCfg<64, 128, 2, 4, 32, true, GATED, AM, EP>>(p, max_mblk, s);
+    case 16: return run<Fp8Cfg<16, 128, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
+    case 32: return run<Fp8Cfg<32, 128, 1, 4, 16, GATED, AM, EP>>(p, max_mblk, s);
+    case 64: return run<Fp8Cfg<64, 128, 2, 4, 32, GATED, AM, EP>>(p, max_mblk, s);
     case 128:
       // first GEMMs only: the 128-row second-GEMM tile keeps two workgroups
       // per CU on two stages (gemm_min_waves_per_eu)
-      if constexpr (EP == EPI_Z)
-        return run_split<Fp8Split<128, 128, 2, 4, 32, GATED, AM, EP>,
-                         Fp8Cfg<128, 128, 2, 4, 32, GATED, AM, EP>>(p, max_mblk, s);
       return run<Fp8Cfg<128, 128, 2, 4, 32, GATED, AM, EP>>(p, max_mblk, s);
     case 256:
       // 256-row tiles exist for the ungated GEMMs only (a gated 256-row
       // tile does not fit the registers)
-      if constexpr (!GATED)
-        return run_split<Fp8Split<256, 128, 2, 4, 32, false, AM, EP>,
-                         Fp8Cfg<256, 128, 2, 4, 32, false, AM, EP>>(p, max_mblk, s);
+      if constexpr (!GATED) return run<Fp8Cfg<256, 128, 2, 4, 32, false, AM, EP>>(p, max_mblk, s);
       return -1;
     default:
       return -1;

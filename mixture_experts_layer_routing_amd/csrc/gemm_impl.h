@@ -52,7 +52,8 @@ enum { A_GATHER = 0, A_ROWS = 1, A_DENSE = 2 };
 enum { EPI_Z = 0, EPI_OUT_ROUTED = 1, EPI_OUT_DENSE = 2 };
 
 template <int BM_, int BNZ_, int WAVES_M_, int WAVES_N_, int MF_, bool FP8_, bool GATED_,
-          int AMODE_, int EPI_, int NSTAGE_ = 2, int RB_ = 128, bool SPLIT_ = false>
+          int AMODE_, int EPI_, int NSTAGE_ = 2, int RB_ = 128, bool SPLIT_ = false,
+          bool SWAP_ = false>
 struct GemmCfg {
   static constexpr int BM = BM_, BNZ = BNZ_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, MF = MF_;
   static constexpr bool FP8 = FP8_, GATED = GATED_;
@@ -68,6 +69,16 @@ struct GemmCfg {
   // re-read by every column tile and mostly come from L2).  NSTAGE is
   // unused then.
   static constexpr bool SPLIT = SPLIT_;
+  // fp8 first GEMMs: the weight fragment is the matrix instruction's first
+  // operand, so the accumulator tile is transposed -- each lane holds one
+  // activation row and 16 output columns of one fragment, and the k-tile's
+  // promotion needs one scale product per fragment instead of one per
+  // accumulator (the products and their rounding are the same).
+  static constexpr bool SWAP = SWAP_;
+  // fp32 z staging row of the fp8 first-GEMM epilogue (floats): one more
+  // than the tile's columns when lanes write down columns (SWAP), which
+  // keeps a wave's stores on distinct banks.
+  static constexpr int ZSTRIDE = SWAP_ ? BNZ_ + 1 : BNZ_;
 };
 
 // gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16 lanes per
@@ -174,6 +185,18 @@ __device__ __forceinline__ int acc_col(int lane) {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Tile row and column of accumulator element v of lane `lane` in fragment
+// (fm, fn) of a wave whose rows start at row_w and columns at col_w; with
+// swapped operands the fragment is transposed.
+template <int MF, bool SWAP>
+__device__ __forceinline__ int acc_tile_row(int row_w, int fm, int v, int lane) {
+  return row_w + fm * MF + (SWAP ? acc_col<MF>(lane) : acc_row<MF>(v, lane));
+}
+template <int MF, bool SWAP>
+__device__ __forceinline__ int acc_tile_col(int col_w, int fn, int v, int lane) {
+  return col_w + fn * MF + (SWAP ? acc_row<MF>(v, lane) : acc_col<MF>(lane));
+}
+
 // 64 lanes x 16 bytes from per-lane global addresses into 1 KB of LDS,
 // lane i landing at lds + 16*i (global_load_lds_dwordx4).
 __device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* lds) {
@@ -217,7 +240,7 @@ struct GemmLds {
   static constexpr int NB = G * C::BNZ;
   static constexpr int A_BYTES = C::BM * C::RB, B_BYTES = NB * C::RB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int EPI_BYTES = (C::EPI == EPI_Z && C::FP8) ? C::BM * C::BNZ * 4 : C::BM * C::BNZ * 2;
+  static constexpr int EPI_BYTES = (C::EPI == EPI_Z && C::FP8) ? C::BM * C::ZSTRIDE * 4 : C::BM * C::BNZ * 2;
   static constexpr int ARING = 2, BRING = 3;
   static constexpr int RING_BYTES = C::SPLIT ? ARING * A_BYTES + BRING * B_BYTES : C::NSTAGE * STAGE;
   static constexpr int SMEM_TILE = cmax(RING_BYTES, EPI_BYTES);
@@ -272,9 +295,11 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   typedef typename M::frag_t frag_t;
   constexpr int NSUB = RB / M::KSTEP, NACC = M::NACC;
   static_assert(NSUB >= 1, "k-tile holds at least one MFMA step");
-  constexpr int EPI_BYTES = (C::EPI == EPI_Z && FP8) ? BM * BNZ * 4 : BM * BNZ * 2;
+  constexpr int EPI_BYTES = (C::EPI == EPI_Z && FP8) ? BM * C::ZSTRIDE * 4 : BM * BNZ * 2;
+  constexpr bool SWAP = C::SWAP;
+  static_assert(!SWAP || (FP8 && C::EPI == EPI_Z && BM < 256), "swapped operands: fp8 first-GEMM tiles");
   constexpr int NSTAGE = C::NSTAGE;
-  static_assert(NSTAGE == 2 || (!FP8 && NI % NW == 0), "deeper pipelines: bf16, whole load groups");
+  static_assert(NSTAGE == 2 || NI % NW == 0, "deeper pipelines: whole load groups");
   constexpr bool SPLIT = C::SPLIT;
   static_assert(!SPLIT || NSTAGE == 2, "split rings replace the stage count");
   constexpr int A_G = BM / RPG, B_G = NB / RPG;          // 1 KB load groups of A and of B rows
@@ -288,6 +313,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   constexpr int kMaxKB = LDS::kMaxKB;
   constexpr int SA_KB = LDS::SA_KB;
   constexpr int SCALE_BYTES = LDS::SCALE_BYTES;
+  static_assert(!FP8 || SA_KB >= NSTAGE, "a ring slot of activation scales per stage");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_TILE + SCALE_BYTES];
   float* const sA = reinterpret_cast<float*>(smem + SMEM_TILE);
   float* const sW = sA + SA_KB * BM;
@@ -528,7 +554,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   // Whole table when it fits; split rings always fit it (the host only
   // picks a split-ring tile when K / 128 / ksplit <= its capacity).
   const bool whole = SPLIT || nk <= SA_KB;
-  // Row r's scale of k-tile kt straight to sA[kt & 1][r] by a 4-byte
+  // Row r's scale of k-tile kt straight to sA[b][r] (ring slot b) by a 4-byte
   // direct-to-LDS load (threads r < BM; lane i of a wave writes 4*i bytes
   // past the wave's base), issued with the k-tile's stage loads.
   auto dma_sa = [&](int kt, int b) {
@@ -578,7 +604,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   };
 
   // One fp8 k-tile (kt, tile-local) from stage buffers As / Bs.
-  auto compute_fp8 = [&](int kt, const uint8_t* As, const uint8_t* Bs, auto full_tag) {
+  auto compute_fp8 = [&](int kt, int slot, const uint8_t* As, const uint8_t* Bs, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     // this k-tile's scales: weight blocks (gate, up) and the rows' activation
     // scales; the latter are read ahead of the MFMAs unless registers are
@@ -586,7 +612,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
     constexpr bool LEAN = gemm_min_waves_per_eu<C>() > 1;
     constexpr bool PER_FRAGMENT = BM >= 256;
     const float swg[2] = {sW[wblk * kMaxKB + kbase + kt], C::GATED ? sW[kMaxKB + kbase + kt] : 0.f};
-    const float* sAb = sA + (whole ? kt : (kt & 1)) * BM;
+    const float* sAb = sA + (whole ? kt : slot) * BM;
     auto read_sa = [&](int fm, float (&out)[NACC]) {
 #pragma unroll
       for (int q = 0; q < NACC / 4; ++q) {
@@ -637,10 +663,16 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       }
       return;
     }
-    float sa[(LEAN || PER_FRAGMENT) ? 1 : FM][NACC];
-    if constexpr (!LEAN && !PER_FRAGMENT) {
+    float sa[(LEAN || PER_FRAGMENT || SWAP) ? 1 : FM][NACC];
+    if constexpr (!LEAN && !PER_FRAGMENT && !SWAP) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) read_sa(fm, sa[fm]);
+    }
+    // swapped operands: this lane's activation row of each row fragment
+    float sa_row[SWAP ? FM : 1];
+    if constexpr (SWAP) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) sa_row[fm] = sAb[row_w + fm * MF + (lane & (MF - 1))];
     }
     acc_t part[G][FM][FN];
 #pragma unroll
@@ -665,8 +697,24 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
 #pragma unroll
                 for (int v = 0; v < NACC; ++v) part[g][fm][fn][v] = 0.f;
               }
-              part[g][fm][fn] = M::mma(fa[fm], fb[g][fn], part[g][fm][fn]);
+              part[g][fm][fn] = SWAP ? M::mma(fb[g][fn], fa[fm], part[g][fm][fn])
+                                     : M::mma(fa[fm], fb[g][fn], part[g][fm][fn]);
             }
+    }
+    if constexpr (SWAP) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        if (!(FULL || fm < fm_live)) continue;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float sc = sa_row[fm] * swg[g];
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int v = 0; v < NACC; ++v) acc[g][fm][fn][v] += part[g][fm][fn][v] * sc;
+        }
+      }
+      return;
     }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
@@ -734,8 +782,8 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
     }
   };
 
-  auto compute = [&](int kt, const uint8_t* As, const uint8_t* Bs, auto full_tag) {
-    if constexpr (FP8) compute_fp8(kt, As, Bs, full_tag);
+  auto compute = [&](int kt, int slot, const uint8_t* As, const uint8_t* Bs, auto full_tag) {
+    if constexpr (FP8) compute_fp8(kt, slot, As, Bs, full_tag);
     else compute_bf16(As, Bs, full_tag);
   };
 
@@ -765,30 +813,47 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
         const int bn2 = bb + 2 >= BRING ? bb + 2 - BRING : bb + 2;
         if (kt + 1 < nk) dma_a(kt + 1, (kt + 1) & 1, full_tag);
         if (kt + 2 < nk) dma_b(kt + 2, bn2);
-        compute(kt, smem + (kt & 1) * A_BYTES, smem + ARING * A_BYTES + bb * B_BYTES, full_tag);
+        compute(kt, kt & 1, smem + (kt & 1) * A_BYTES, smem + ARING * A_BYTES + bb * B_BYTES, full_tag);
         bb = bb + 1 == BRING ? 0 : bb + 1;
       }
       return;
     }
     if constexpr (FP8) {
-      static_assert(!FP8 || NSTAGE == 2, "fp8 runs two LDS stages");
-      if (nk > 0) {
-        if (!whole) dma_sa(0, 0);
-        dma(0, 0, full_tag);
-      }
+      // As the generic loop below, plus the activation scales: the whole
+      // table before the loop, or one 4-byte direct load per row and k-tile
+      // into ring slot kt % NSTAGE, issued with the k-tile's stage loads by
+      // the waves that hold rows (< BM), which then count one load more per
+      // k-tile.
+#pragma unroll
+      for (int st = 0; st < NSTAGE - 1; ++st)
+        if (st < nk) {
+          if (!whole) dma_sa(st, st);
+          dma(st, st, full_tag);
+        }
       load_scale_table();
-      int buf = 0;
+      const bool sa_wave = !whole && wave * 64 < BM;
+      int buf = 0, nbuf = NSTAGE - 1;
       for (int kt = 0; kt < nk; ++kt) {
         // k-tile kt's loads (stage and scales) have landed
-        wait_vm_loads();
-        lds_barrier();
-        if (kt + 1 < nk) {
-          // buffer (kt+1)&1 was last read in iteration kt-1, before this barrier
-          if (!whole) dma_sa(kt + 1, (kt + 1) & 1);
-          dma(kt + 1, buf ^ 1, full_tag);
+        if constexpr (NSTAGE > 2) {
+          if (kt + NSTAGE - 2 < nk) {
+            if (sa_wave) wait_vm_loads_but<(NIW + 1) * (NSTAGE - 2)>();
+            else wait_vm_loads_but<NIW * (NSTAGE - 2)>();
+          } else {
+            wait_vm_loads();
+          }
+        } else {
+          wait_vm_loads();
         }
-        compute(kt, smem + buf * STAGE, smem + buf * STAGE + A_BYTES, full_tag);
-        buf ^= 1;
+        lds_barrier();
+        if (kt + NSTAGE - 1 < nk) {
+          // slot nbuf was last read in iteration kt-1, before this barrier
+          if (!whole) dma_sa(kt + NSTAGE - 1, nbuf);
+          dma(kt + NSTAGE - 1, nbuf, full_tag);
+        }
+        compute(kt, buf, smem + buf * STAGE, smem + buf * STAGE + A_BYTES, full_tag);
+        buf = buf + 1 == NSTAGE ? 0 : buf + 1;
+        nbuf = nbuf + 1 == NSTAGE ? 0 : nbuf + 1;
       }
       return;
     }
@@ -808,7 +873,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       }
       lds_barrier();
       if (kt + NSTAGE - 1 < nk) dma(kt + NSTAGE - 1, nbuf, full_tag);
-      compute(kt, smem + buf * STAGE, smem + buf * STAGE + A_BYTES, full_tag);
+      compute(kt, buf, smem + buf * STAGE, smem + buf * STAGE + A_BYTES, full_tag);
       buf = buf + 1 == NSTAGE ? 0 : buf + 1;
       nbuf = nbuf + 1 == NSTAGE ? 0 : nbuf + 1;
     }
@@ -830,9 +895,9 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
           for (int v = 0; v < NACC; ++v) {
-            const int r = row_w + fm * MF + acc_row<MF>(v, lane);
+            const int r = acc_tile_row<MF, SWAP>(row_w, fm, v, lane);
             if (r < row_end) {
-              const int cc = wn * WN + fn * MF + acc_col<MF>(lane);
+              const int cc = acc_tile_col<MF, SWAP>(wn * WN, fn, v, lane);
               const int prow = p.part_flat ? p.sorted[m0 + r] : m0 + r;
               part[static_cast<int64_t>(prow) * p.ldp + g * p.inter + n0 + cc] =
                   acc[g][fm][fn][v];
@@ -849,12 +914,12 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int v = 0; v < NACC; ++v) {
-          const int r = row_w + fm * MF + acc_row<MF>(v, lane);
-          const int cc = wn * WN + fn * MF + acc_col<MF>(lane);
+          const int r = acc_tile_row<MF, SWAP>(row_w, fm, v, lane);
+          const int cc = acc_tile_col<MF, SWAP>(wn * WN, fn, v, lane);
           float z;
           if constexpr (C::GATED) z = act_apply(p.act, acc[0][fm][fn][v]) * acc[G - 1][fm][fn][v];
           else z = act_apply(p.act, acc[0][fm][fn][v]);
-          if constexpr (FP8) reinterpret_cast<float*>(smem)[r * BNZ + cc] = z;
+          if constexpr (FP8) reinterpret_cast<float*>(smem)[r * C::ZSTRIDE + cc] = z;
           else reinterpret_cast<uint16_t*>(smem)[r * BNZ + cc] = static_cast<uint16_t>(f32_to_bf16_hw(z));
         }
     __syncthreads();
@@ -866,7 +931,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       for (int i = 0; i < (BM + RPP - 1) / RPP; ++i) {
         const int r = (tid >> 4) + RPP * i;
         if (r < BM) {  // uniform per 16-lane group
-          const float* zr = reinterpret_cast<const float*>(smem) + r * BNZ + ch * 8;
+          const float* zr = reinterpret_cast<const float*>(smem) + r * C::ZSTRIDE + ch * 8;
           float f[8];
           float amax = 0.f;
 #pragma unroll

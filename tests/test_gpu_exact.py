@@ -92,6 +92,10 @@ EXACT_SHAPES = [
     # several 256-row blocks per expert: the bf16 256-row tiles on two stages
     # (fewer rows per expert take the 3-deep weight ring)
     dict(name="exact_tall", T=700, H=256, I=128, E=2, top_k=1, shared_I=128),
+    # long K: more k-tiles than the three-stage fp8 tiles' activation-scale
+    # table holds (GEMM-1 33, GEMM-2 16), so the scales come by per-k-tile
+    # loads into a ring
+    dict(name="exact_long_k", T=300, H=4224, I=2048, E=2, top_k=1, shared_I=256),
 ]
 
 
