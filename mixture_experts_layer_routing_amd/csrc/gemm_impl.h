@@ -565,6 +565,27 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       __builtin_amdgcn_global_load_lds(g, (lds_void*)(sA + b * BM + (tid & ~63)), 4, 0, 0);
     }
   };
+  // Chunked (swapped tiles whose table does not fit, G(128) scales, whole
+  // 16-byte chunks): row r's scales of k-tiles 4c..4c+3 are contiguous, so
+  // one 16-byte direct load per row brings four k-tiles -- a quarter of the
+  // line requests of the per-k-tile loads.  Chunk c goes to ring slot
+  // c % NCH, laid out [row][4]; at the top of k-tile 4c (c >= 1) the slot of
+  // chunk c-1 is free and chunk c-1+NCH is loaded into it, NCH-1 chunks
+  // ahead of its use.
+  constexpr int NCH = (SA_KB / 4) < 8 ? (SA_KB / 4) : 8;
+  const int nchunks = nk / 4;
+  const bool chunked = SWAP && !whole && NCH >= 2 && p.sa_k == 1 && (nk & 3) == 0 &&
+                       (kbase & 3) == 0 && (p.sa_row & 3) == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.a_scale) & 15) == 0;
+  auto dma_chunk = [&](int c) {
+    if (tid < BM) {
+      typedef __attribute__((address_space(3))) void lds_void;
+      const float* g = p.a_scale + static_cast<int64_t>(a_srow) * p.sa_row + kbase + 4 * c;
+      __builtin_amdgcn_global_load_lds(g, (lds_void*)(sA + (c % NCH) * BM * 4 + (tid & ~63) * 4), 16, 0, 0);
+    }
+  };
+  // the chunk (if any) issued at the top of k-tile kt
+  auto chunk_at = [&](int kt) { return (kt > 0 && (kt & 3) == 0) ? kt / 4 - 1 + NCH : -1; };
   // Whole table: thread r < BM loads its row's scales of this tile's
   // k-tiles (16-byte loads where the row's G(128) scales are contiguous and
   // aligned) and stores them to sA[kt][r]; the first barrier publishes them.
@@ -671,8 +692,12 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
     // swapped operands: this lane's activation row of each row fragment
     float sa_row[SWAP ? FM : 1];
     if constexpr (SWAP) {
+      const float* sAc = sA + ((kt >> 2) % NCH) * BM * 4 + (kt & 3);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) sa_row[fm] = sAb[row_w + fm * MF + (lane & (MF - 1))];
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = row_w + fm * MF + (lane & (MF - 1));
+        sa_row[fm] = chunked ? sAc[r * 4] : sAb[r];
+      }
     }
     acc_t part[G][FM][FN];
 #pragma unroll
@@ -824,20 +849,28 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       // into ring slot kt % NSTAGE, issued with the k-tile's stage loads by
       // the waves that hold rows (< BM), which then count one load more per
       // k-tile.
+      if (chunked)
+        for (int c = 0; c < NCH && c < nchunks; ++c) dma_chunk(c);
 #pragma unroll
       for (int st = 0; st < NSTAGE - 1; ++st)
         if (st < nk) {
-          if (!whole) dma_sa(st, st);
+          if (!whole && !chunked) dma_sa(st, st);
           dma(st, st, full_tag);
         }
       load_scale_table();
-      const bool sa_wave = !whole && wave * 64 < BM;
+      const bool row_wave = wave * 64 < BM;
+      const bool sa_wave = !whole && !chunked && row_wave;
       int buf = 0, nbuf = NSTAGE - 1;
       for (int kt = 0; kt < nk; ++kt) {
-        // k-tile kt's loads (stage and scales) have landed
+        // k-tile kt's loads (stage and scales) have landed: at most the
+        // loads issued after them are still in flight -- the later stages',
+        // and a chunk issued at the top of k-tile kt-1 (NSTAGE 3)
         if constexpr (NSTAGE > 2) {
+          static_assert(NSTAGE == 3 || !SWAP, "chunk accounting assumes three stages");
+          const bool chunk_prev = chunked && row_wave && chunk_at(kt - 1) >= 0 &&
+                                  chunk_at(kt - 1) < nchunks;
           if (kt + NSTAGE - 2 < nk) {
-            if (sa_wave) wait_vm_loads_but<(NIW + 1) * (NSTAGE - 2)>();
+            if (sa_wave || chunk_prev) wait_vm_loads_but<(NIW + 1) * (NSTAGE - 2)>();
             else wait_vm_loads_but<NIW * (NSTAGE - 2)>();
           } else {
             wait_vm_loads();
@@ -846,9 +879,14 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
           wait_vm_loads();
         }
         lds_barrier();
+        if (chunked) {
+          // chunk kt/4 - 1 (k-tiles up to kt-1) was last read before this barrier
+          const int c = chunk_at(kt);
+          if (c >= 0 && c < nchunks) dma_chunk(c);
+        }
         if (kt + NSTAGE - 1 < nk) {
           // slot nbuf was last read in iteration kt-1, before this barrier
-          if (!whole) dma_sa(kt + NSTAGE - 1, nbuf);
+          if (!whole && !chunked) dma_sa(kt + NSTAGE - 1, nbuf);
           dma(kt + NSTAGE - 1, nbuf, full_tag);
         }
         compute(kt, buf, smem + buf * STAGE, smem + buf * STAGE + A_BYTES, full_tag);

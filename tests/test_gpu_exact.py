@@ -96,6 +96,9 @@ EXACT_SHAPES = [
     # table holds (GEMM-1 33, GEMM-2 16), so the scales come by per-k-tile
     # loads into a ring
     dict(name="exact_long_k", T=300, H=4224, I=2048, E=2, top_k=1, shared_I=256),
+    # 32 k-tiles: the swapped three-stage tiles take the scales four k-tiles
+    # per load, into a ring of chunks
+    dict(name="exact_scale_chunks", T=300, H=4096, I=1024, E=2, top_k=1, shared_I=256),
 ]
 
 
