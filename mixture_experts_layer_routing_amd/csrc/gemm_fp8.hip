@@ -28,10 +28,9 @@ static int run(const GemmParams* p, int64_t max_mblk, hipStream_t s) {
 // T=8192 2.03 -> 2.15 ms).
 constexpr int fp8_stages(int bm, int ep) { return bm == 128 && ep == EPI_Z ? 3 : 2; }
 
-// First GEMMs below 256 rows run with swapped operands (GemmCfg::SWAP).
+// Every fp8 tile runs with swapped operands (GemmCfg::SWAP).
 template <int BM, int BNZ, int WM, int WN, int MF, bool GATED, int AM, int EP>
-using Fp8Cfg = GemmCfg<BM, BNZ, WM, WN, MF, true, GATED, AM, EP, fp8_stages(BM, EP), 128, false,
-                       EP == EPI_Z && BM < 256>;
+using Fp8Cfg = GemmCfg<BM, BNZ, WM, WN, MF, true, GATED, AM, EP, fp8_stages(BM, EP), 128, false, true>;
 
 template <int AM, int EP, bool GATED>
 static int dispatch_bm(int block_m, const GemmParams* p, int64_t max_mblk, hipStream_t s) {
@@ -57,8 +56,8 @@ static int dispatch_bm(int block_m, const GemmParams* p, int64_t max_mblk, hipSt
 // wave's 64 columns stay inside one 128-row weight-scale block.
 template <int AM, int EP>
 static int dispatch_wide(int block_m, const GemmParams* p, int64_t max_mblk, hipStream_t s) {
-  if (block_m == 16) return run<GemmCfg<16, 256, 1, 4, 16, true, false, AM, EP>>(p, max_mblk, s);
-  if (block_m == 32) return run<GemmCfg<32, 256, 1, 4, 16, true, false, AM, EP>>(p, max_mblk, s);
+  if (block_m == 16) return run<Fp8Cfg<16, 256, 1, 4, 16, false, AM, EP>>(p, max_mblk, s);
+  if (block_m == 32) return run<Fp8Cfg<32, 256, 1, 4, 16, false, AM, EP>>(p, max_mblk, s);
   return -1;
 }
 

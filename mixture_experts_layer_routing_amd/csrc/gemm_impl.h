@@ -69,16 +69,18 @@ struct GemmCfg {
   // re-read by every column tile and mostly come from L2).  NSTAGE is
   // unused then.
   static constexpr bool SPLIT = SPLIT_;
-  // fp8 first GEMMs: the weight fragment is the matrix instruction's first
+  // fp8 tiles: the weight fragment is the matrix instruction's first
   // operand, so the accumulator tile is transposed -- each lane holds one
   // activation row and 16 output columns of one fragment, and the k-tile's
   // promotion needs one scale product per fragment instead of one per
   // accumulator (the products and their rounding are the same).
   static constexpr bool SWAP = SWAP_;
-  // fp32 z staging row of the fp8 first-GEMM epilogue (floats): one more
+  // Epilogue staging rows: fp32 z of the fp8 first GEMM (floats), one more
   // than the tile's columns when lanes write down columns (SWAP), which
-  // keeps a wave's stores on distinct banks.
+  // keeps a wave's stores on distinct banks; bf16 y (elements), eight more
+  // (a 16-byte row shift) for the same reason, rows staying 16-byte aligned.
   static constexpr int ZSTRIDE = SWAP_ ? BNZ_ + 1 : BNZ_;
+  static constexpr int YSTRIDE = SWAP_ ? BNZ_ + 8 : BNZ_;
 };
 
 // gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16 lanes per
@@ -240,7 +242,7 @@ struct GemmLds {
   static constexpr int NB = G * C::BNZ;
   static constexpr int A_BYTES = C::BM * C::RB, B_BYTES = NB * C::RB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int EPI_BYTES = (C::EPI == EPI_Z && C::FP8) ? C::BM * C::ZSTRIDE * 4 : C::BM * C::BNZ * 2;
+  static constexpr int EPI_BYTES = (C::EPI == EPI_Z && C::FP8) ? C::BM * C::ZSTRIDE * 4 : C::BM * C::YSTRIDE * 2;
   static constexpr int ARING = 2, BRING = 3;
   static constexpr int RING_BYTES = C::SPLIT ? ARING * A_BYTES + BRING * B_BYTES : C::NSTAGE * STAGE;
   static constexpr int SMEM_TILE = cmax(RING_BYTES, EPI_BYTES);
@@ -295,9 +297,9 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   typedef typename M::frag_t frag_t;
   constexpr int NSUB = RB / M::KSTEP, NACC = M::NACC;
   static_assert(NSUB >= 1, "k-tile holds at least one MFMA step");
-  constexpr int EPI_BYTES = (C::EPI == EPI_Z && FP8) ? BM * C::ZSTRIDE * 4 : BM * BNZ * 2;
+  constexpr int EPI_BYTES = (C::EPI == EPI_Z && FP8) ? BM * C::ZSTRIDE * 4 : BM * C::YSTRIDE * 2;
   constexpr bool SWAP = C::SWAP;
-  static_assert(!SWAP || (FP8 && C::EPI == EPI_Z && BM < 256), "swapped operands: fp8 first-GEMM tiles");
+  static_assert(!SWAP || FP8, "swapped operands: fp8 tiles");
   constexpr int NSTAGE = C::NSTAGE;
   static_assert(NSTAGE == 2 || NI % NW == 0, "deeper pipelines: whole load groups");
   constexpr bool SPLIT = C::SPLIT;
@@ -669,8 +671,22 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
 #pragma unroll
                 for (int v = 0; v < NACC; ++v) pf[g][fn][v] = 0.f;
               }
-              pf[g][fn] = M::mma(fa, fb[s][g][fn], pf[g][fn]);
+              pf[g][fn] = SWAP ? M::mma(fb[s][g][fn], fa, pf[g][fn]) : M::mma(fa, fb[s][g][fn], pf[g][fn]);
             }
+        }
+        if constexpr (SWAP) {
+          // this lane's activation row of the fragment: one scale product
+          const int r = row_w + fm * MF + (lane & (MF - 1));
+          const float sa1 = chunked ? sA[((kt >> 2) % NCH) * BM * 4 + r * 4 + (kt & 3)] : sAb[r];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float sc = sa1 * swg[g];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+              for (int v = 0; v < NACC; ++v) acc[g][fm][fn][v] += pf[g][fn][v] * sc;
+          }
+          continue;
         }
         float sr[NACC];
         read_sa(fm, sr);
@@ -1011,9 +1027,9 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int v = 0; v < NACC; ++v) {
-          const int r = row_w + fm * MF + acc_row<MF>(v, lane);
-          const int cc = wn * WN + fn * MF + acc_col<MF>(lane);
-          reinterpret_cast<uint16_t*>(smem)[r * BNZ + cc] =
+          const int r = acc_tile_row<MF, SWAP>(row_w, fm, v, lane);
+          const int cc = acc_tile_col<MF, SWAP>(wn * WN, fn, v, lane);
+          reinterpret_cast<uint16_t*>(smem)[r * C::YSTRIDE + cc] =
               static_cast<uint16_t>(f32_to_bf16_hw(acc[0][fm][fn][v]));
         }
     __syncthreads();
@@ -1024,7 +1040,7 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       int orow;
       if constexpr (C::EPI == EPI_OUT_ROUTED) orow = p.sorted[m0 + r];
       else orow = m0 + r;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + (r * BNZ + ch * 8) * 2);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + (r * C::YSTRIDE + ch * 8) * 2);
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + static_cast<int64_t>(orow) * p.ldo +
                                 n0 + ch * 8) = v;
     }
