@@ -836,9 +836,12 @@ __global__ __launch_bounds__(kResThreads) void align_resident_kernel(
                  sorted);
 }
 
-// ---- decode prologue: routing and align in one wave (T*top_k <= 64) ------
+// ---- decode prologue: routing and align in one wave (T <= 8, T*top_k <= 64)
 // Decode-sized batches spend more time launching the routing and align
-// kernels than computing them; this one wave does both.  Lane l of the wave
+// kernels than computing them; this one wave does both.  It routes its
+// tokens in batches of TB with their cross-lane steps interleaved, but a
+// wave still spends about a microsecond per token on them, so past 8
+// tokens the two launches (one wave per token) are faster.  Lane l of the wave
 // then holds flat row l's expert: one peer mask per lane gives the counts
 // (its leader's popcount) and the stable slots (peers below); the padded
 // offsets are a wave scan over the experts; pad slots and the tail get the
@@ -847,8 +850,9 @@ __global__ __launch_bounds__(kResThreads) void align_resident_kernel(
 // needed between its LDS writes and reads.
 constexpr int kPrologueMaxIds = 64;
 constexpr int kPrologueMaxE = 1024;
+constexpr int kPrologueMaxTokens = 8;
 
-template <int VPL>
+template <int VPL, int TB>
 __global__ __launch_bounds__(64) void decode_prologue_kernel(
     const float* __restrict__ logits, int T, int E, int top_k, int scoring, int renorm,
     int32_t* __restrict__ ids, float* __restrict__ weights, int nbits, int BM,
@@ -860,14 +864,31 @@ __global__ __launch_bounds__(64) void decode_prologue_kernel(
   __shared__ int off[kPrologueMaxE + 1];
   const int lane = threadIdx.x;
   const int n = T * top_k;
-  for (int t = 0; t < T; ++t) {
-    int e;
-    float w;
-    route_token<VPL>(logits + static_cast<size_t>(t) * E, E, top_k, scoring, renorm, &e, &w);
-    if (lane < top_k) {
-      ids[t * top_k + lane] = e;
-      weights[t * top_k + lane] = w;
-      flat[t * top_k + lane] = e;
+  // the tokens' logits in batches of TB (one round trip per batch), then the
+  // batch's top-k with the tokens' cross-lane steps interleaved (padding
+  // tokens of the last batch hold -inf and are not stored)
+  for (int t0 = 0; t0 < T; t0 += TB) {
+    float v[TB][VPL];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      if (t0 + b < T) {
+        load_logits<VPL>(logits + static_cast<size_t>(t0 + b) * E, E, v[b]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) v[b][i] = -__builtin_inff();
+      }
+    }
+    int e[TB];
+    float w[TB];
+    route_logits<VPL, TB>(v, E, top_k, scoring, renorm, e, w);
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      const int t = t0 + b;
+      if (t < T && lane < top_k) {
+        ids[t * top_k + lane] = e[b];
+        weights[t * top_k + lane] = w[b];
+        flat[t * top_k + lane] = e[b];
+      }
     }
   }
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
@@ -1084,8 +1105,8 @@ void launch_align(const int32_t* ids, int64_t n, int E, int BM, int32_t* counts,
 }
 
 bool decode_prologue_fits(int T, int top_k, int E, int64_t sorted_cap) {
-  return static_cast<int64_t>(T) * top_k <= kPrologueMaxIds && E <= kPrologueMaxE &&
-         sorted_cap <= 16384;
+  return T <= kPrologueMaxTokens && static_cast<int64_t>(T) * top_k <= kPrologueMaxIds &&
+         E <= kPrologueMaxE && sorted_cap <= 16384;
 }
 
 void launch_decode_prologue(const float* logits, int T, int E, int top_k, int scoring,
@@ -1093,10 +1114,20 @@ void launch_decode_prologue(const float* logits, int T, int E, int top_k, int sc
                             int32_t* offsets, int32_t* sorted, int64_t sorted_cap,
                             int32_t* block_ids, int64_t block_cap, int32_t* ntp, hipStream_t s) {
   const int nbits = ceil_log2(E);
+  // batch: the tokens' count rounded up to a power of two, at most 8/VPL
+  // logits registers' worth (8 for E <= 64)
   auto go = [&](auto vpl) {
-    decode_prologue_kernel<decltype(vpl)::value><<<1, 64, 0, s>>>(
-        logits, T, E, top_k, scoring, renorm, ids, weights, nbits, BM, counts, offsets, sorted,
-        sorted_cap, block_ids, block_cap, ntp);
+    constexpr int V = decltype(vpl)::value;
+    auto run = [&](auto tb) {
+      decode_prologue_kernel<V, decltype(tb)::value><<<1, 64, 0, s>>>(
+          logits, T, E, top_k, scoring, renorm, ids, weights, nbits, BM, counts, offsets, sorted,
+          sorted_cap, block_ids, block_cap, ntp);
+    };
+    constexpr int cap = V >= 8 ? 1 : 8 / V;
+    if (T <= 1 || cap == 1) run(std::integral_constant<int, 1>{});
+    else if (T <= 2 || cap == 2) run(std::integral_constant<int, (cap >= 2 ? 2 : 1)>{});
+    else if (T <= 4 || cap == 4) run(std::integral_constant<int, (cap >= 4 ? 4 : 1)>{});
+    else run(std::integral_constant<int, (cap >= 8 ? 8 : 1)>{});
   };
   if (E <= 64) go(std::integral_constant<int, 1>{});
   else if (E <= 128) go(std::integral_constant<int, 2>{});

@@ -17,7 +17,7 @@ void launch_prepare(const uint16_t* a1, int T, int H, const float* w, int apply_
 size_t align_workspace_bytes(int64_t n, int E);
 // Routing and align of a decode-sized batch in one launch (one wave), with
 // the outputs of launch_route and launch_align; only where
-// decode_prologue_fits (T*top_k <= 64, E <= 1024, sorted capacity <= 16384).
+// decode_prologue_fits (T <= 8, T*top_k <= 64, E <= 1024, sorted capacity <= 16384).
 bool decode_prologue_fits(int T, int top_k, int E, int64_t sorted_cap);
 void launch_decode_prologue(const float* logits, int T, int E, int top_k, int scoring,
                             int renorm, int32_t* ids, float* weights, int BM, int32_t* counts,
