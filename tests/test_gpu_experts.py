@@ -237,8 +237,13 @@ def test_forward_reduced(spec):
     ("decode_split_mini", {}), ("decode_split_fp8_mini", {}), ("decode_split_no_mul_mini", {}),
     ("decode_split_mini", {"residual": True, "out_quant": "fp8"}),
     ("decode_split_fp8_mini", {"residual": True, "rmsnorm": True}),
-    ("fp8_out_mini", {}), ("llama4_mini", {}), ("finalize_fused_mini", {})],
-    ids=lambda v: v if isinstance(v, str) else "+".join(v) or "plain")
+    ("fp8_out_mini", {}), ("llama4_mini", {}), ("finalize_fused_mini", {}),
+    # one-wave decode prologue routing several tokens per batch: E = 128
+    # (batches of 4, the last one padded), 256 (batches of 2) and 1024 (one)
+    ("tiny", {"T": 7, "E": 128, "top_k": 4}),
+    ("tiny", {"T": 8, "E": 256, "top_k": 8, "scoring": "sigmoid"}),
+    ("tiny", {"T": 6, "E": 1024, "top_k": 2, "renormalize": False})],
+    ids=lambda v: v if isinstance(v, str) else "+".join(f"{k}{x}" for k, x in v.items()) or "plain")
 def test_forward_equals_the_staged_calls(name, extra):
     """moe_forward is, bit for bit, the composition of the staged calls:
     route -> prepare -> align -> experts -> finalize.  That holds where a
