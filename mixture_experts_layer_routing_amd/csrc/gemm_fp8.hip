@@ -6,7 +6,8 @@
 // 4 waves split along N, BM 64/128/256 use 32x32x64 MFMA on 2x4 waves (two
 // per SIMD).  256-row tiles serve the second GEMM (and ungated first GEMMs):
 // the gated first GEMM would need a partial set beside 2 x 128 accumulators
-// per lane, which spills, so it runs two 128-row tiles per 256-row block.
+// per lane, which spills (swapped and promoted fragment by fragment too), so
+// it runs two 128-row tiles per 256-row block.
 #include "gemm_impl.h"
 
 namespace moe {
