@@ -453,6 +453,11 @@ def test_forward_full_size_sampled(spec):
     got = _out_f64(spec, out, scale, sample)
     fp8 = spec.quant.startswith("fp8")
     if fp8:
+        # max-norm here: the derived per-element fp8 allowance walks every
+        # touched expert's weights in float64 (about 220 experts for the
+        # sampled tokens, minutes of host time); the per-element fp8 checks
+        # at full size are the stage checks on sampled experts
+        # (test_experts_full_size_fp8_stages)
         allowance = None
     else:
         allowance = routed_allowance(spec, dict(refs["mirrored"], x_bits=x_bits), hw,
