@@ -392,6 +392,40 @@ int moe_forward_graph_launch(moe_graph* graph, hipStream_t stream);
 int moe_forward_graph_destroy(moe_graph* graph);
 
 /*
+ * moe_forward_monolithic -- the whole layer as ONE kernel launch, for
+ * decode-sized batches: the monolithic mode of "[vLLM] MoE Oracle &
+ * Prepare/Finalize" (section on modular vs monolithic kernels: the monolithic
+ * mode fuses routing, the experts and finalize into a single kernel instead
+ * of the modular chain of stages).  One persistent launch runs routing, both
+ * GEMMs of the routed and the shared experts and finalize, with grid-wide
+ * barriers between the phases, so its workgroups must all be resident at
+ * once: one per CU the stream may use.
+ *   Arguments as moe_forward (no block_m, no stage events), with these
+ *   limits: bf16 weights (quant MOE_QUANT_NONE), 1 <= T <= 64,
+ *   T*top_k <= 64; out_quant MOE_QUANT_NONE or MOE_QUANT_FP8_G128.
+ *   workspace (device): at least moe_forward_monolithic_workspace_bytes.
+ *   The result equals moe_forward's up to the summation order of the GEMMs
+ *   (fp32 sums of the same bf16 products, rounded once to bf16).
+ * Errors: moe_forward's argument checks; MOE_ERR_UNSUPPORTED outside the
+ * limits above, on a stream under graph capture (each launch carries a
+ * fresh barrier epoch, which a replay would repeat), or when the kernel
+ * cannot place a workgroup on the stream's CUs; MOE_ERR_WORKSPACE.  Nothing
+ * is enqueued on an error.  The barriers' waits are bounded (about a second
+ * each): if the grid cannot become resident (another process holding CUs),
+ * the launch gives up and leaves output unwritten.
+ */
+int moe_forward_monolithic(const uint16_t* x, const float* logits, int T, int H, int top_k,
+                           int scoring, int renormalize, int apply_router_weight_on_input,
+                           const moe_weights* weights /* host */, int activation,
+                           const uint16_t* residual, const uint16_t* gamma, float eps,
+                           int out_quant, void* output, float* output_scale,
+                           uint16_t* residual_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+/* (host) workspace moe_forward_monolithic needs for these sizes. */
+size_t moe_forward_monolithic_workspace_bytes(int T, int H, int top_k,
+                                              const moe_weights* weights, int activation);
+
+/*
  * moe_forward_noalloc -- moe_forward for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same layer, arguments and results as moe_forward,

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     moe_experts_workspace_layout,
     moe_finalize,
     moe_forward,
+    moe_forward_monolithic,
     moe_forward_noalloc,
     moe_forward_workspace_bytes,
     moe_pick_block_m,

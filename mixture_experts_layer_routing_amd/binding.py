@@ -109,6 +109,11 @@ def _load():
                                              ctypes.POINTER(MoeWeights), c_int, c_int, c_vp, c_vp,
                                              c_f32, c_int, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp,
                                              ctypes.POINTER(c_vp)]),
+        "moe_forward_monolithic": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                           ctypes.POINTER(MoeWeights), c_int, c_vp, c_vp, c_f32,
+                                           c_int, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+        "moe_forward_monolithic_workspace_bytes": (c_sz, [c_int, c_int, c_int,
+                                                          ctypes.POINTER(MoeWeights), c_int]),
         "moe_forward_graph_launch": (c_int, [c_vp, c_vp]),
         "moe_forward_graph_destroy": (c_int, [c_vp]),
     }
@@ -375,6 +380,32 @@ def moe_forward(x, logits, weights, top_k, scoring="softmax", renormalize=True,
                             float(eps), QUANT[out_quant], _ptr(output), _ptr(output_scale),
                             _ptr(residual_out), _ptr(workspace), wsb, ev, _stream(stream)),
            "moe_forward")
+    return output, (output_scale if out_quant == "fp8" else None), workspace
+
+
+def moe_forward_monolithic(x, logits, weights, top_k, scoring="softmax", renormalize=True,
+                           apply_router_weight_on_input=False, activation="silu", residual=None,
+                           gamma=None, eps=1e-6, out_quant="none", output=None, output_scale=None,
+                           residual_out=None, workspace=None, stream=None):
+    """The whole layer as one kernel launch (bf16 weights, T <= 64,
+    T*top_k <= 64); arguments and results as moe_forward."""
+    T, H = x.shape
+    dev = x.device
+    if output is None:
+        output = torch.empty((T, H), dtype=torch.uint8 if out_quant == "fp8" else torch.bfloat16,
+                             device=dev)
+    if out_quant == "fp8" and output_scale is None:
+        output_scale = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+    wsb = _lib.moe_forward_monolithic_workspace_bytes(T, H, top_k, ctypes.byref(weights),
+                                                      ACTIVATION[activation])
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(_lib.moe_forward_monolithic(
+        _ptr(x), _ptr(logits), T, H, top_k, SCORING[scoring], int(renormalize),
+        int(apply_router_weight_on_input), ctypes.byref(weights), ACTIVATION[activation],
+        _ptr(residual), _ptr(gamma), float(eps), QUANT[out_quant], _ptr(output),
+        _ptr(output_scale), _ptr(residual_out), _ptr(workspace), wsb, _stream(stream)),
+        "moe_forward_monolithic")
     return output, (output_scale if out_quant == "fp8" else None), workspace
 
 

@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["route.hip", "prepare.hip", "align.hip", "finalize.hip", "splitk.hip", "batched.hip",
-           "gemm_bf16.hip", "gemm_fp8.hip", "moe_api.cpp"]
+           "gemm_bf16.hip", "gemm_fp8.hip", "monolithic.hip", "moe_api.cpp"]
 
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 

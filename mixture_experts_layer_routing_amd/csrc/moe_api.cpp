@@ -1039,6 +1039,74 @@ int moe_forward_graph_destroy(moe_graph* graph) {
 
 }  // extern "C"
 
+// ---- moe_forward_monolithic: the layer in one launch ----
+
+size_t moe_forward_monolithic_workspace_bytes(int T, int H, int top_k, const moe_weights* weights,
+                                              int activation) {
+  if (!weights || T <= 0 || top_k <= 0 || H <= 0) return 0;
+  (void)activation;
+  return moe::monolithic_workspace_bytes(T, H, top_k, weights->inter,
+                                         std::max(weights->shared_inter, 0));
+}
+
+int moe_forward_monolithic(const uint16_t* x, const float* logits, int T, int H, int top_k,
+                           int scoring, int renormalize, int apply_router_weight_on_input,
+                           const moe_weights* weights, int activation, const uint16_t* residual,
+                           const uint16_t* gamma, float eps, int out_quant, void* output,
+                           float* output_scale, uint16_t* residual_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int bm = 0;
+  if (int st = forward_args(x, logits, T, H, top_k, scoring, apply_router_weight_on_input,
+                            weights, activation, 0, eps, out_quant, output, output_scale, &bm))
+    return st;
+  if (T == 0) return MOE_OK;
+  if (weights->quant != MOE_QUANT_NONE)
+    return fail(MOE_ERR_UNSUPPORTED, "the one-launch layer takes bf16 weights only");
+  if (!moe::monolithic_fits(T, top_k))
+    return fail(MOE_ERR_UNSUPPORTED, "the one-launch layer needs T <= 64 and T*top_k <= 64 (T=%d, top_k=%d)",
+                T, top_k);
+  const size_t need = moe_forward_monolithic_workspace_bytes(T, H, top_k, weights, activation);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "one-launch workspace %zu < %zu", workspace_bytes, need);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_HIP, "hipStreamIsCapturing failed");
+  }
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(MOE_ERR_UNSUPPORTED, "the one-launch layer cannot be captured into a graph");
+  moe::MonoLaunch m{};
+  m.x = x;
+  m.logits = logits;
+  m.T = T;
+  m.H = H;
+  m.E = weights->num_experts;
+  m.top_k = top_k;
+  m.scoring = scoring;
+  m.renorm = renormalize ? 1 : 0;
+  m.woi = apply_router_weight_on_input ? 1 : 0;
+  m.act = act_fn(activation);
+  m.gated = act_gated(activation) ? 1 : 0;
+  m.w13 = static_cast<const uint16_t*>(weights->w13);
+  m.w2 = static_cast<const uint16_t*>(weights->w2);
+  m.I = weights->inter;
+  m.sw13 = static_cast<const uint16_t*>(weights->shared_w13);
+  m.sw2 = static_cast<const uint16_t*>(weights->shared_w2);
+  m.Is = std::max(weights->shared_inter, 0);
+  m.residual = residual;
+  m.gamma = gamma;
+  m.eps = eps;
+  m.out_fp8 = out_quant == MOE_QUANT_FP8_G128 ? 1 : 0;
+  m.out = output;
+  m.out_scale = output_scale;
+  m.residual_out = residual_out;
+  m.ws = workspace;
+  if (moe::launch_monolithic(m, stream) != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "the one-launch kernel does not fit the stream's CUs");
+  return check_launch("moe_forward_monolithic");
+}
+
 // ---- moe_forward_noalloc: the forward on a fixed scratch array ----
 //
 // One array per GPU, defined here, held by each GPU the library runs on

@@ -1,0 +1,508 @@
+// The whole layer in one launch for decode-sized batches: the monolithic
+// mode of "[vLLM] MoE Oracle & Prepare/Finalize" (section on modular vs
+// monolithic kernels: the monolithic mode fuses routing, the experts and
+// finalize into a single kernel), for bf16 weights, T <= 64 and T*top_k <= 64.
+//
+// One persistent launch, one 512-thread workgroup per CU the stream may use
+// (all resident at once), four phases with a grid barrier between each two
+// (grid_sync.h: per-workgroup arrival flags tagged with a per-call epoch,
+// bounded waits):
+//   A  routing: wave t routes token t (route_token, as the routing kernel),
+//      ids and weights to the workspace.
+//   B  first GEMMs: every workgroup sorts the T*top_k routed rows by expert
+//      in LDS (flat-index order within an expert, as align orders them).
+//      Work items, one wave each: (touched expert, 16 z columns) and
+//      (shared expert, 16 z columns).
+//   C  second GEMMs: (touched expert, 16 H columns), (shared expert, 16 H
+//      columns).
+//   D  finalize: workgroup g finalizes tokens g, g+G, ... (weighted sum of
+//      the token's rows, shared row, residual, optional RMSNorm, bf16 or
+//      fp8 G(128) output), as the finalize kernel.
+// A wave computes its 16 output columns for up to 16 rows at a time with
+// 16x16x32 bf16 MFMAs, the weight rows as first operand (lane r of lane
+// group q holds K elements [32s + 8q, +8) of weight row r and of activation
+// row r), both operands loaded from global memory straight into registers,
+// one batch of k-steps ahead: at decode sizes each weight byte is read once
+// and the activation rows (a few KB) come from the L2, so nothing is staged
+// in LDS.  Each output is a plain fp32 sum over K of bf16 products, rounded
+// once to bf16 (z after the activation, y) -- the modular path's arithmetic
+// in another summation order.
+#include "moe_device.h"
+#include "launch.h"
+#include "route_device.h"
+#include "grid_sync.h"
+
+#include <algorithm>
+
+namespace moe {
+namespace {
+
+constexpr int kMonoThreads = 512, kMonoWaves = kMonoThreads / 64;
+constexpr int kMonoMaxRows = 64;      // T * top_k
+constexpr int kMonoMaxGrid = kMonoThreads;   // arrival flags (workgroup 0 polls one a thread)
+
+struct MonoArgs {
+  const uint16_t* x;
+  const float* logits;
+  int T, H, E, top_k, scoring, renorm, woi, act, gated;
+  const uint16_t* w13;    // [E][G*I][H]
+  const uint16_t* w2;     // [E][H][I]
+  int I;
+  const uint16_t* sw13;   // shared expert [G*Is][H], or null
+  const uint16_t* sw2;    // [H][Is]
+  int Is;
+  const uint16_t* residual;
+  const uint16_t* gamma;
+  float eps;
+  int out_fp8;
+  void* out;
+  float* out_scale;
+  uint16_t* residual_out;
+  // workspace
+  int32_t* ids;           // [T*top_k]
+  float* wts;             // [T*top_k]
+  uint16_t* z;            // [T*top_k][I]
+  uint16_t* zsh;          // [T][Is]
+  uint16_t* y;            // [T*top_k][H]
+  uint16_t* ysh;          // [T][H]
+  uint64_t* flags;        // [kMonoMaxGrid] arrival flags, then the go word
+  uint64_t epoch;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// bf16(f32(v) * s) of 8 packed bf16 values (weight on the input: the
+// product of two bf16 numbers is exact in f32, one rounding).
+__device__ __forceinline__ u32x4 scale8(u32x4 v, float s) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32_to_bf16(bf16_to_f32(v[i]) * s) | (f32_to_bf16(bf16_to_f32(v[i] >> 16) * s) << 16);
+  return o;
+}
+
+// One wave: acc[g][v] += sum over K of a[row r16][k] * w_g[4q + v][k] for the
+// lane's activation row (arow, or zeros when null) and G weight rows (the
+// lane's row r16 of each 16-row fragment).  K a multiple of 32 * U.  aw: the
+// activation multiplier (weight on the input), applied when woi.
+template <int G, int U>
+__device__ __forceinline__ void wave_gemm(const uint16_t* arow, bool woi, float aw,
+                                          const uint16_t* const (&wrow)[G], int K, int q,
+                                          f32x4 (&acc)[G]) {
+  u32x4 A[2][U], W[2][U][G];
+  const int nb = K / (32 * U);
+  auto load = [&](int b, int buf) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (b * U + u) * 32 + 8 * q;
+      A[buf][u] = arow ? ld16(arow + k) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int g = 0; g < G; ++g) W[buf][u][g] = ld16(wrow[g] + k);
+    }
+  };
+  auto comp = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4 a = woi ? scale8(A[buf][u], aw) : A[buf][u];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, W[buf][u][g]),
+                                                         __builtin_bit_cast(bf16x8_t, a), acc[g], 0, 0, 0);
+    }
+  };
+  load(0, 0);
+  for (int b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) load(b + 1, 1);
+    comp(0);
+    if (b + 1 < nb) {
+      if (b + 2 < nb) load(b + 2, 0);
+      comp(1);
+    }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void wave_gemm_k(const uint16_t* arow, bool woi, float aw,
+                                            const uint16_t* const (&wrow)[G], int K, int q,
+                                            f32x4 (&acc)[G]) {
+  if (K % 128 == 0) wave_gemm<G, 4>(arow, woi, aw, wrow, K, q, acc);
+  else wave_gemm<G, 2>(arow, woi, aw, wrow, K, q, acc);
+}
+
+// The routed rows sorted by expert (LDS, built by wave 0): rows[p] is the
+// p-th flat row t*top_k+j in expert order, flat order within an expert;
+// expert s of the touched ones is slot_e[s], its rows rows[slot_off[s] ..
+// slot_off[s+1]).
+struct RowTable {
+  int rows[kMonoMaxRows];
+  int slot_e[kMonoMaxRows];
+  int slot_off[kMonoMaxRows + 1];
+  int ids[kMonoMaxRows];
+  int n_slots;
+};
+
+__device__ void build_rows(const MonoArgs& a, RowTable& tb) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = a.T * a.top_k;
+  if (tid < 64) tb.ids[lane] = lane < n ? a.ids[lane] : 0x7fffffff;
+  __syncthreads();
+  if (tid < 64) {
+    const int my = tb.ids[lane];
+    int less = 0, before = 0;
+    for (int j = 0; j < n; ++j) {
+      const int o = tb.ids[j];
+      less += o < my;
+      before += (o == my) & (j < lane);
+    }
+    if (lane < n) tb.rows[less + before] = lane;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int e = lane < n ? tb.ids[tb.rows[lane]] : -1;
+    const int prev = (lane > 0 && lane < n) ? tb.ids[tb.rows[lane - 1]] : -2;
+    const bool first = lane < n && e != prev;
+    const uint64_t m = __ballot(first);
+    const int slot = __builtin_popcountll(m & lanemask_lt());
+    if (first) {
+      tb.slot_e[slot] = e;
+      tb.slot_off[slot] = lane;
+    }
+    if (lane == 0) {
+      tb.n_slots = __builtin_popcountll(m);
+      tb.slot_off[__builtin_popcountll(m)] = n;
+    }
+  }
+  __syncthreads();
+}
+
+// Phase B: first GEMMs.  Item i < n_slots * I/16: touched expert i / (I/16),
+// z columns 16 (i mod I/16) ..; then the shared expert's Is/16 items.
+template <int G>
+__device__ void phase_gemm1(const MonoArgs& a, const RowTable& tb, int gw, int nw) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
+  const int cw = a.I / 16, cs = a.Is / 16;
+  const int routed = tb.n_slots * cw;
+  const int total = routed + (a.sw13 ? cs : 0);
+  for (int it = gw; it < total; it += nw) {
+    const bool shared = it >= routed;
+    const int s = shared ? 0 : it / cw;
+    const int c = shared ? it - routed : it % cw;
+    const int In = shared ? a.Is : a.I;
+    const uint16_t* wb = shared ? a.sw13
+                                : a.w13 + static_cast<int64_t>(tb.slot_e[s]) * G * a.I * a.H;
+    const uint16_t* wrow[G];
+    wrow[0] = wb + static_cast<int64_t>(16 * c + r16) * a.H;
+    if constexpr (G == 2) wrow[1] = wb + static_cast<int64_t>(In + 16 * c + r16) * a.H;
+    const int nrows = shared ? a.T : tb.slot_off[s + 1] - tb.slot_off[s];
+    for (int r0 = 0; r0 < nrows; r0 += 16) {
+      const int rr = r0 + r16;
+      int flat = -1, tok = -1;
+      if (rr < nrows) {
+        flat = shared ? rr : tb.rows[tb.slot_off[s] + rr];
+        tok = shared ? rr : flat / a.top_k;
+      }
+      const bool woi = a.woi && !shared;   // the shared expert reads the unweighted input
+      float aw = 1.0f;
+      if (woi && flat >= 0) aw = bf16_to_f32(f32_to_bf16(a.wts[flat]));
+      f32x4 acc[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      wave_gemm_k<G>(tok >= 0 ? a.x + static_cast<int64_t>(tok) * a.H : nullptr, woi, aw, wrow,
+                     a.H, q, acc);
+      if (rr < nrows) {
+        uint16_t* zr = (shared ? a.zsh + static_cast<int64_t>(rr) * a.Is
+                               : a.z + static_cast<int64_t>(flat) * a.I) + 16 * c + 4 * q;
+        float zv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          zv[v] = G == 2 ? act_apply(a.act, acc[0][v]) * acc[G - 1][v] : act_apply(a.act, acc[0][v]);
+        u32x2 pk;
+        pk[0] = f32_to_bf16_hw(zv[0]) | (f32_to_bf16_hw(zv[1]) << 16);
+        pk[1] = f32_to_bf16_hw(zv[2]) | (f32_to_bf16_hw(zv[3]) << 16);
+        *reinterpret_cast<u32x2*>(zr) = pk;
+      }
+    }
+  }
+}
+
+// Phase C: second GEMMs.  Item i < n_slots * H/16: touched expert i / (H/16),
+// H columns 16 (i mod H/16) ..; then the shared expert's H/16 items.
+__device__ void phase_gemm2(const MonoArgs& a, const RowTable& tb, int gw, int nw) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
+  const int ch = a.H / 16;
+  const int routed = tb.n_slots * ch;
+  const int total = routed + (a.sw2 ? ch : 0);
+  for (int it = gw; it < total; it += nw) {
+    const bool shared = it >= routed;
+    const int s = shared ? 0 : it / ch;
+    const int c = shared ? it - routed : it % ch;
+    const int K = shared ? a.Is : a.I;
+    const uint16_t* wb = shared ? a.sw2 : a.w2 + static_cast<int64_t>(tb.slot_e[s]) * a.H * a.I;
+    const uint16_t* wrow[1] = {wb + static_cast<int64_t>(16 * c + r16) * K};
+    const int nrows = shared ? a.T : tb.slot_off[s + 1] - tb.slot_off[s];
+    for (int r0 = 0; r0 < nrows; r0 += 16) {
+      const int rr = r0 + r16;
+      int flat = -1;
+      if (rr < nrows) flat = shared ? rr : tb.rows[tb.slot_off[s] + rr];
+      const uint16_t* arow = nullptr;
+      if (flat >= 0) arow = shared ? a.zsh + static_cast<int64_t>(flat) * a.Is
+                                   : a.z + static_cast<int64_t>(flat) * a.I;
+      f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+      wave_gemm_k<1>(arow, false, 1.0f, wrow, K, q, acc);
+      if (flat >= 0) {
+        uint16_t* yr = (shared ? a.ysh : a.y) + static_cast<int64_t>(flat) * a.H + 16 * c + 4 * q;
+        u32x2 pk;
+        pk[0] = f32_to_bf16_hw(acc[0][0]) | (f32_to_bf16_hw(acc[0][1]) << 16);
+        pk[1] = f32_to_bf16_hw(acc[0][2]) | (f32_to_bf16_hw(acc[0][3]) << 16);
+        *reinterpret_cast<u32x2*>(yr) = pk;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack8f(u32x4 r, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(r[i]);
+    f[2 * i + 1] = bf16_to_f32(r[i] >> 16);
+  }
+}
+
+// Phase D: finalize of token t by the workgroup; thread tid owns the
+// 8-column chunks tid + 512 i.  acc = sum_j w'_j y[t, j] (slot order; w' = 1
+// with the weight on the input) + shared row + residual; residual_out =
+// bf16(acc); with gamma, out = acc * (1 / sqrt(mean(acc^2) + eps)) * gamma;
+// bf16 out, or E4M3 with one scale per 128 columns.
+__device__ void finalize_token(const MonoArgs& a, int t, float* part) {
+  constexpr int MAXC = 4;                   // H <= 16384
+  const int tid = threadIdx.x;
+  const int nch = a.H / 8;
+  const int64_t row = static_cast<int64_t>(t) * a.H;
+  float acc[MAXC][8];
+  float sumsq = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = tid + kMonoThreads * i;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[i][v] = 0.f;
+    if (c < nch) {
+      for (int j = 0; j < a.top_k; ++j) {
+        const int f = t * a.top_k + j;
+        const float wj = a.woi ? 1.0f : a.wts[f];
+        float yv[8];
+        unpack8f(ld16(a.y + static_cast<int64_t>(f) * a.H + c * 8), yv);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[i][v] += wj * yv[v];
+      }
+      if (a.sw2) {
+        float sv[8];
+        unpack8f(ld16(a.ysh + row + c * 8), sv);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[i][v] += sv[v];
+      }
+      if (a.residual) {
+        float rv[8];
+        unpack8f(ld16(a.residual + row + c * 8), rv);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[i][v] += rv[v];
+      }
+      if (a.residual_out) {
+        u32x4 o;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(acc[i][2 * h], acc[i][2 * h + 1]);
+        *reinterpret_cast<u32x4*>(a.residual_out + row + c * 8) = o;
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) sumsq += acc[i][v] * acc[i][v];
+    }
+  }
+  float r = 1.0f;
+  if (a.gamma) {
+    const float ws = wave_sum(sumsq);
+    if ((tid & 63) == 0) part[tid >> 6] = ws;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMonoWaves; ++w) tot += part[w];
+    __syncthreads();                        // part is reused by the next token
+    r = 1.0f / sqrtf(tot / static_cast<float>(a.H) + a.eps);
+  }
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = tid + kMonoThreads * i;
+    float o[8];
+    if (c < nch && a.gamma) {
+      float g[8];
+      unpack8f(ld16(a.gamma + c * 8), g);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) o[v] = acc[i][v] * r * g[v];
+    } else {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) o[v] = acc[i][v];
+    }
+    if (a.out_fp8) {
+      // nch is a multiple of 16 (H % 128 == 0): 16-lane groups are uniform
+      if (kMonoThreads * i < nch) {
+        float amax = 0.f;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) amax = fmaxf(amax, __builtin_fabsf(o[v]));
+        amax = group_max<16>(amax);
+        const float s = fmaxf(amax, kQuantEps) / kFp8Max;
+        if (c < nch) {
+          u32x2 qv;
+          qv[0] = pack4_e4m3(o[0] / s, o[1] / s, o[2] / s, o[3] / s);
+          qv[1] = pack4_e4m3(o[4] / s, o[5] / s, o[6] / s, o[7] / s);
+          *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.out) + row + c * 8) = qv;
+          if ((tid & 15) == 0) a.out_scale[static_cast<int64_t>(t) * (a.H / 128) + (c >> 4)] = s;
+        }
+      }
+    } else if (c < nch) {
+      u32x4 ov;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) ov[h] = pack_bf16x2(o[2 * h], o[2 * h + 1]);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + row + c * 8) = ov;
+    }
+  }
+}
+
+template <int VPL, int G>
+__global__ __launch_bounds__(kMonoThreads) void moe_monolithic_kernel(MonoArgs a) {
+  __shared__ RowTable tb;
+  __shared__ float part[kMonoWaves];
+  __shared__ int okf;
+  const int g = blockIdx.x, G_ = gridDim.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gw = g * kMonoWaves + wave, nw = G_ * kMonoWaves;
+  uint64_t* flags = a.flags;
+  uint64_t* go = a.flags + kMonoMaxGrid;
+
+  // A: routing, one wave per token
+  for (int t = gw; t < a.T; t += nw) {
+    int e;
+    float w;
+    route_token<VPL>(a.logits + static_cast<int64_t>(t) * a.E, a.E, a.top_k, a.scoring, a.renorm,
+                     &e, &w);
+    if (lane < a.top_k) {
+      a.ids[t * a.top_k + lane] = e;
+      a.wts[t * a.top_k + lane] = w;
+    }
+  }
+  __syncthreads();
+  grid_arrive(flags, a.epoch + 1, g);
+  if (!grid_await(flags, go, a.epoch + 1, g, G_, &okf)) return;
+
+  // B: first GEMMs
+  build_rows(a, tb);
+  phase_gemm1<G>(a, tb, gw, nw);
+  __syncthreads();
+  grid_arrive(flags, a.epoch + 2, g);
+  if (!grid_await(flags, go, a.epoch + 2, g, G_, &okf)) return;
+
+  // C: second GEMMs
+  phase_gemm2(a, tb, gw, nw);
+  __syncthreads();
+  grid_arrive(flags, a.epoch + 3, g);
+  if (!grid_await(flags, go, a.epoch + 3, g, G_, &okf)) return;
+
+  // D: finalize
+  for (int t = g; t < a.T; t += G_) finalize_token(a, t, part);
+}
+
+template <int VPL>
+void launch_vpl(const MonoArgs& a, int grid, hipStream_t s) {
+  if (a.gated) moe_monolithic_kernel<VPL, 2><<<grid, kMonoThreads, 0, s>>>(a);
+  else moe_monolithic_kernel<VPL, 1><<<grid, kMonoThreads, 0, s>>>(a);
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+bool monolithic_fits(int T, int top_k) {
+  return T >= 1 && T <= 64 && static_cast<int64_t>(T) * top_k <= kMonoMaxRows;
+}
+
+size_t monolithic_workspace_bytes(int T, int H, int top_k, int I, int Is) {
+  const size_t n = static_cast<size_t>(T) * top_k;
+  return align_up((kMonoMaxGrid + 1) * sizeof(uint64_t)) + align_up(n * 4) * 2 +
+         align_up(n * I * 2) + align_up(static_cast<size_t>(T) * Is * 2) + align_up(n * H * 2) +
+         align_up(static_cast<size_t>(T) * H * 2);
+}
+
+// Workgroups the launch may use: one per CU of the stream's CU mask (the
+// kernel fits a CU), 0 if it does not fit at all.
+int monolithic_grid(hipStream_t s) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, moe_monolithic_kernel<16, 2>, kMonoThreads,
+                                                   0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, moe_monolithic_kernel<16, 1>, kMonoThreads,
+                                                   0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (nb < 1) return 0;
+  uint32_t mask[32] = {};
+  if (hipExtStreamGetCUMask(s, 32, mask) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int cus = 0;
+  for (uint32_t m : mask) cus += __builtin_popcount(m);
+  return std::min(cus, kMonoMaxGrid);
+}
+
+int launch_monolithic(const MonoLaunch& m, hipStream_t s) {
+  const int grid = monolithic_grid(s);
+  if (grid <= 0) return -1;
+  MonoArgs a{};
+  a.x = m.x;
+  a.logits = m.logits;
+  a.T = m.T;
+  a.H = m.H;
+  a.E = m.E;
+  a.top_k = m.top_k;
+  a.scoring = m.scoring;
+  a.renorm = m.renorm;
+  a.woi = m.woi;
+  a.act = m.act;
+  a.gated = m.gated;
+  a.w13 = m.w13;
+  a.w2 = m.w2;
+  a.I = m.I;
+  a.sw13 = m.Is > 0 ? m.sw13 : nullptr;
+  a.sw2 = m.Is > 0 ? m.sw2 : nullptr;
+  a.Is = m.Is;
+  a.residual = m.residual;
+  a.gamma = m.gamma;
+  a.eps = m.eps;
+  a.out_fp8 = m.out_fp8;
+  a.out = m.out;
+  a.out_scale = m.out_scale;
+  a.residual_out = m.residual_out;
+  const size_t n = static_cast<size_t>(m.T) * m.top_k;
+  uint8_t* p = static_cast<uint8_t*>(m.ws);
+  a.flags = reinterpret_cast<uint64_t*>(p);
+  p += align_up((kMonoMaxGrid + 1) * sizeof(uint64_t));
+  a.ids = reinterpret_cast<int32_t*>(p);
+  p += align_up(n * 4);
+  a.wts = reinterpret_cast<float*>(p);
+  p += align_up(n * 4);
+  a.z = reinterpret_cast<uint16_t*>(p);
+  p += align_up(n * m.I * 2);
+  a.zsh = reinterpret_cast<uint16_t*>(p);
+  p += align_up(static_cast<size_t>(m.T) * m.Is * 2);
+  a.y = reinterpret_cast<uint16_t*>(p);
+  p += align_up(n * m.H * 2);
+  a.ysh = reinterpret_cast<uint16_t*>(p);
+  a.epoch = next_epoch() & ~static_cast<uint64_t>(3);
+  if (m.E <= 64) launch_vpl<1>(a, grid, s);
+  else if (m.E <= 128) launch_vpl<2>(a, grid, s);
+  else if (m.E <= 256) launch_vpl<4>(a, grid, s);
+  else if (m.E <= 512) launch_vpl<8>(a, grid, s);
+  else launch_vpl<16>(a, grid, s);
+  return 0;
+}
+
+}  // namespace moe
