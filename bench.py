@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--fp8-leg", default="deepseek_v3@T8192",
                     help="second workload timed in the same run (the fp8 path); 'none' to skip")
+    ap.add_argument("--decode-leg", default="mixtral@T1",
+                    help="decode-sized workload timed in the same run three ways: eager "
+                         "moe_forward, its graph replay, and the one-launch layer; 'none' to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay leg (counter passes profile eager launches only)")
@@ -356,6 +359,27 @@ def measure(a, torch, moe, spec, block_m=0, graph=True):
         graph_ms = gstart.elapsed_time(gstop) / a.steps
         g.close()
         del g
+    # the one-launch layer (moe_forward_monolithic), where it applies: bf16
+    # weights, T <= 64, T*top_k <= 64
+    mono_ms = None
+    if graph and spec.quant == "none" and spec.T <= 64 and spec.T * spec.top_k <= 64:
+        def mono(out_m=None, ws_m=None):
+            return moe.moe_forward_monolithic(
+                d["x"], d["logits"], w, spec.top_k, spec.scoring, spec.renormalize,
+                spec.apply_router_weight_on_input, spec.activation, d.get("residual"),
+                d.get("gamma"), spec.eps, spec.out_quant, output=out_m, workspace=ws_m)
+        mout, _, mws = mono()
+        for _ in range(a.warmup):
+            mono(mout, mws)
+        torch.cuda.synchronize()
+        mstart, mstop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        mstart.record(stream)
+        for _ in range(a.steps):
+            mono(mout, mws)
+        mstop.record(stream)
+        torch.cuda.synchronize()
+        mono_ms = mstart.elapsed_time(mstop) / a.steps
+        del mout, mws
     stage = {}
     for j in range(1, moe.NUM_STAGE_EVENTS):
         vals = [evs[i][j - 1].elapsed_time(evs[i][j]) for i in range(a.steps)]
@@ -368,7 +392,7 @@ def measure(a, torch, moe, spec, block_m=0, graph=True):
     g1_tflops = gemm1_flops(spec) / (g1_ms * 1e-3) / 1e12
     roof = layer_roofline(spec, touched)
     res = {
-        "ms": ms, "wall": wall, "bm": bm, "stage": stage, "graph_ms": graph_ms,
+        "ms": ms, "wall": wall, "bm": bm, "stage": stage, "graph_ms": graph_ms, "mono_ms": mono_ms,
         "tflops": (routed + shared) / (ms * 1e-3) / 1e12, "dtype": dtype,
         "g1_ms": g1_ms, "g1_tflops": g1_tflops, "layer_roofline": roof,
         # GEMM-1's weights streamed once: the HBM floor of that kernel
@@ -470,6 +494,21 @@ def main():
                              hbm_floor_frac=round(fres["g1_hbm_floor_ms"] / fres["g1_ms"], 4)),
         }
         del fd, fkeep
+        torch.cuda.empty_cache()
+    if a.decode_leg != "none" and a.decode_leg != spec.name:
+        # a decode step three ways: eager launches, one graph launch of the
+        # same kernels, and the one-launch layer (one persistent kernel)
+        dspec = find_spec(a.decode_leg)
+        dres, dd_, dkeep = measure(a, torch, moe, dspec, 0, graph=True)
+        line["decode_leg"] = {
+            "workload": dspec.name, "block_m": dres["bm"],
+            "eager_ms": round(dres["ms"], 4),
+            "graph_ms": None if dres["graph_ms"] is None else round(dres["graph_ms"], 4),
+            "one_launch_ms": None if dres["mono_ms"] is None else round(dres["mono_ms"], 4),
+            "layer_roofline_ms": round(dres["layer_roofline"]["ms"], 4),
+            "stage_ms": {k: round(v, 4) for k, v in dres["stage"].items()},
+        }
+        del dd_, dkeep
         torch.cuda.empty_cache()
     if not a.no_hbm_stages:
         line.update(hbm_stages(torch, moe, dev))

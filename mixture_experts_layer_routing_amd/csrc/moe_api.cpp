@@ -12,6 +12,7 @@
 #include <new>
 
 #include "launch.h"
+#include "monolithic.h"
 
 namespace {
 

@@ -29,6 +29,7 @@
 // in another summation order.
 #include "moe_device.h"
 #include "launch.h"
+#include "monolithic.h"
 #include "route_device.h"
 #include "grid_sync.h"
 
@@ -40,6 +41,7 @@ namespace {
 constexpr int kMonoThreads = 512, kMonoWaves = kMonoThreads / 64;
 constexpr int kMonoMaxRows = 64;      // T * top_k
 constexpr int kMonoMaxGrid = kMonoThreads;   // arrival flags (workgroup 0 polls one a thread)
+constexpr int kMonoMaxSplit = 8;     // K split of the second GEMMs
 
 struct MonoArgs {
   const uint16_t* x;
@@ -63,8 +65,8 @@ struct MonoArgs {
   float* wts;             // [T*top_k]
   uint16_t* z;            // [T*top_k][I]
   uint16_t* zsh;          // [T][Is]
-  uint16_t* y;            // [T*top_k][H]
-  uint16_t* ysh;          // [T][H]
+  float* yp;              // second-GEMM partials [S][T*top_k][H]
+  float* yshp;            // [S][T][H]
   uint64_t* flags;        // [kMonoMaxGrid] arrival flags, then the go word
   uint64_t epoch;
 };
@@ -83,21 +85,30 @@ __device__ __forceinline__ u32x4 scale8(u32x4 v, float s) {
   return o;
 }
 
-// One wave: acc[g][v] += sum over K of a[row r16][k] * w_g[4q + v][k] for the
-// lane's activation row (arow, or zeros when null) and G weight rows (the
-// lane's row r16 of each 16-row fragment).  K a multiple of 32 * U.  aw: the
-// activation multiplier (weight on the input), applied when woi.
-template <int G, int U>
-__device__ __forceinline__ void wave_gemm(const uint16_t* arow, bool woi, float aw,
-                                          const uint16_t* const (&wrow)[G], int K, int q,
+// One wave: acc[g][v] += sum over k in [k0, k0 + K) of a[row r16][k] *
+// w_g[4q + v][k] for the lane's activation row arow and G weight rows (the
+// lane's row r16 of each 16-row fragment).  Output column r16 depends on
+// activation row r16 alone, so lanes without a row of their own read any
+// valid row and leave their column unstored.  K a
+// multiple of 32 * U.  WOI: the activation row is first multiplied by aw
+// and rounded to bf16 (weight on the input).  Batches of U k-steps in a ring
+// of three: two batches load while one feeds the MFMAs.  Inside the main
+// loop every batch issues its loads (past the last batch they fetch the
+// last one again, into a slot that is not read), so the compiler's count of
+// the loads in flight stays exact across the loop and its waits cover only
+// the batch about to be used.
+template <int G, int U, bool WOI>
+__device__ __forceinline__ void wave_gemm(const uint16_t* arow, float aw,
+                                          const uint16_t* const (&wrow)[G], int k0, int K, int q,
                                           f32x4 (&acc)[G]) {
-  u32x4 A[2][U], W[2][U][G];
+  u32x4 A[3][U], W[3][U][G];
   const int nb = K / (32 * U);
   auto load = [&](int b, int buf) {
+    b = min(b, nb - 1);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = (b * U + u) * 32 + 8 * q;
-      A[buf][u] = arow ? ld16(arow + k) : u32x4{0u, 0u, 0u, 0u};
+      const int k = k0 + (b * U + u) * 32 + 8 * q;
+      A[buf][u] = ld16(arow + k);
 #pragma unroll
       for (int g = 0; g < G; ++g) W[buf][u][g] = ld16(wrow[g] + k);
     }
@@ -105,7 +116,7 @@ __device__ __forceinline__ void wave_gemm(const uint16_t* arow, bool woi, float 
   auto comp = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const u32x4 a = woi ? scale8(A[buf][u], aw) : A[buf][u];
+      const u32x4 a = WOI ? scale8(A[buf][u], aw) : A[buf][u];
 #pragma unroll
       for (int g = 0; g < G; ++g)
         acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, W[buf][u][g]),
@@ -113,22 +124,27 @@ __device__ __forceinline__ void wave_gemm(const uint16_t* arow, bool woi, float 
     }
   };
   load(0, 0);
-  for (int b = 0; b < nb; b += 2) {
-    if (b + 1 < nb) load(b + 1, 1);
+  load(1, 1);
+  int b = 0;
+  for (; b + 3 <= nb; b += 3) {
+    load(b + 2, 2);
     comp(0);
-    if (b + 1 < nb) {
-      if (b + 2 < nb) load(b + 2, 0);
-      comp(1);
-    }
+    load(b + 3, 0);
+    comp(1);
+    load(b + 4, 1);
+    comp(2);
   }
+  // the last nb mod 3 batches: b in slot 0, b+1 in slot 1
+  if (b < nb) comp(0);
+  if (b + 1 < nb) comp(1);
 }
 
-template <int G>
-__device__ __forceinline__ void wave_gemm_k(const uint16_t* arow, bool woi, float aw,
-                                            const uint16_t* const (&wrow)[G], int K, int q,
+template <int G, bool WOI>
+__device__ __forceinline__ void wave_gemm_k(const uint16_t* arow, float aw,
+                                            const uint16_t* const (&wrow)[G], int k0, int K, int q,
                                             f32x4 (&acc)[G]) {
-  if (K % 128 == 0) wave_gemm<G, 4>(arow, woi, aw, wrow, K, q, acc);
-  else wave_gemm<G, 2>(arow, woi, aw, wrow, K, q, acc);
+  if (K % 128 == 0) wave_gemm<G, 4, WOI>(arow, aw, wrow, k0, K, q, acc);
+  else wave_gemm<G, 2, WOI>(arow, aw, wrow, k0, K, q, acc);
 }
 
 // The routed rows sorted by expert (LDS, built by wave 0): rows[p] is the
@@ -141,9 +157,10 @@ struct RowTable {
   int slot_off[kMonoMaxRows + 1];
   int ids[kMonoMaxRows];
   int n_slots;
+  int ksplit;           // the second GEMMs' K split (see phase_gemm2)
 };
 
-__device__ void build_rows(const MonoArgs& a, RowTable& tb) {
+__device__ void build_rows(const MonoArgs& a, RowTable& tb, int nw) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = a.T * a.top_k;
   if (tid < 64) tb.ids[lane] = lane < n ? a.ids[lane] : 0x7fffffff;
@@ -170,8 +187,19 @@ __device__ void build_rows(const MonoArgs& a, RowTable& tb) {
       tb.slot_off[slot] = lane;
     }
     if (lane == 0) {
-      tb.n_slots = __builtin_popcountll(m);
-      tb.slot_off[__builtin_popcountll(m)] = n;
+      const int ns = __builtin_popcountll(m);
+      tb.n_slots = ns;
+      tb.slot_off[ns] = n;
+      // Second GEMMs: split K in S (a power of two up to 8) while the items
+      // still fit the waves and every slice stays whole 64-deep batches --
+      // at T = 1 the H/16 column items of one or two experts leave most
+      // waves idle otherwise.
+      const int items = (ns + (a.sw2 ? 1 : 0)) * (a.H / 16);
+      int S = 1;
+      while (S < kMonoMaxSplit && items * S * 2 <= nw && a.I % (2 * S * 64) == 0 &&
+             (!a.sw2 || a.Is % (2 * S * 64) == 0))
+        S *= 2;
+      tb.ksplit = S;
     }
   }
   __syncthreads();
@@ -209,8 +237,10 @@ __device__ void phase_gemm1(const MonoArgs& a, const RowTable& tb, int gw, int n
       f32x4 acc[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      wave_gemm_k<G>(tok >= 0 ? a.x + static_cast<int64_t>(tok) * a.H : nullptr, woi, aw, wrow,
-                     a.H, q, acc);
+      // (lanes without a row read token 0; their column is not stored)
+      const uint16_t* arow = a.x + static_cast<int64_t>(tok >= 0 ? tok : 0) * a.H;
+      if (woi) wave_gemm_k<G, true>(arow, aw, wrow, 0, a.H, q, acc);
+      else wave_gemm_k<G, false>(arow, aw, wrow, 0, a.H, q, acc);
       if (rr < nrows) {
         uint16_t* zr = (shared ? a.zsh + static_cast<int64_t>(rr) * a.Is
                                : a.z + static_cast<int64_t>(flat) * a.I) + 16 * c + 4 * q;
@@ -227,18 +257,25 @@ __device__ void phase_gemm1(const MonoArgs& a, const RowTable& tb, int gw, int n
   }
 }
 
-// Phase C: second GEMMs.  Item i < n_slots * H/16: touched expert i / (H/16),
-// H columns 16 (i mod H/16) ..; then the shared expert's H/16 items.
+// Phase C: second GEMMs in fp32 partials over S slices of K (S =
+// tb.ksplit).  Item i < n_slots * H/16 * S: slice i mod S of touched expert
+// (i / S) / (H/16), H columns 16 ((i / S) mod H/16) ..; then the shared
+// expert's H/16 * S items.  Finalize sums the slices in order and rounds once
+// to bf16, the value of an unsplit sum up to its order.
 __device__ void phase_gemm2(const MonoArgs& a, const RowTable& tb, int gw, int nw) {
   const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
-  const int ch = a.H / 16;
-  const int routed = tb.n_slots * ch;
-  const int total = routed + (a.sw2 ? ch : 0);
+  const int ch = a.H / 16, S = tb.ksplit;
+  const int n = a.T * a.top_k;
+  const int routed = tb.n_slots * ch * S;
+  const int total = routed + (a.sw2 ? ch * S : 0);
   for (int it = gw; it < total; it += nw) {
     const bool shared = it >= routed;
-    const int s = shared ? 0 : it / ch;
-    const int c = shared ? it - routed : it % ch;
+    const int j = shared ? it - routed : it;
+    const int sp = j % S, rest = j / S;
+    const int s = shared ? 0 : rest / ch;
+    const int c = shared ? rest : rest % ch;
     const int K = shared ? a.Is : a.I;
+    const int Ks = K / S;
     const uint16_t* wb = shared ? a.sw2 : a.w2 + static_cast<int64_t>(tb.slot_e[s]) * a.H * a.I;
     const uint16_t* wrow[1] = {wb + static_cast<int64_t>(16 * c + r16) * K};
     const int nrows = shared ? a.T : tb.slot_off[s + 1] - tb.slot_off[s];
@@ -246,19 +283,33 @@ __device__ void phase_gemm2(const MonoArgs& a, const RowTable& tb, int gw, int n
       const int rr = r0 + r16;
       int flat = -1;
       if (rr < nrows) flat = shared ? rr : tb.rows[tb.slot_off[s] + rr];
-      const uint16_t* arow = nullptr;
-      if (flat >= 0) arow = shared ? a.zsh + static_cast<int64_t>(flat) * a.Is
-                                   : a.z + static_cast<int64_t>(flat) * a.I;
+      // (lanes without a row read the group's first row; not stored)
+      const int src = flat >= 0 ? flat : (shared ? 0 : tb.rows[tb.slot_off[s]]);
+      const uint16_t* arow = shared ? a.zsh + static_cast<int64_t>(src) * a.Is
+                                    : a.z + static_cast<int64_t>(src) * a.I;
       f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-      wave_gemm_k<1>(arow, false, 1.0f, wrow, K, q, acc);
+      wave_gemm_k<1, false>(arow, 1.0f, wrow, sp * Ks, Ks, q, acc);
       if (flat >= 0) {
-        uint16_t* yr = (shared ? a.ysh : a.y) + static_cast<int64_t>(flat) * a.H + 16 * c + 4 * q;
-        u32x2 pk;
-        pk[0] = f32_to_bf16_hw(acc[0][0]) | (f32_to_bf16_hw(acc[0][1]) << 16);
-        pk[1] = f32_to_bf16_hw(acc[0][2]) | (f32_to_bf16_hw(acc[0][3]) << 16);
-        *reinterpret_cast<u32x2*>(yr) = pk;
+        float* yr = shared ? a.yshp + (static_cast<int64_t>(sp) * a.T + flat) * a.H
+                           : a.yp + (static_cast<int64_t>(sp) * n + flat) * a.H;
+        *reinterpret_cast<f32x4*>(yr + 16 * c + 4 * q) = acc[0];
       }
     }
+  }
+}
+
+// 8 columns of a second-GEMM output row from its S fp32 slices: summed in
+// slice order, rounded to bf16 (the layer's y), returned as floats.
+__device__ __forceinline__ void y8(const float* p, int64_t slice_stride, int S, float* f) {
+  f32x4 lo = *reinterpret_cast<const f32x4*>(p), hi = *reinterpret_cast<const f32x4*>(p + 4);
+  for (int sp = 1; sp < S; ++sp) {
+    lo += *reinterpret_cast<const f32x4*>(p + sp * slice_stride);
+    hi += *reinterpret_cast<const f32x4*>(p + sp * slice_stride + 4);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    f[v] = bf16_to_f32(f32_to_bf16_hw(lo[v]));
+    f[4 + v] = bf16_to_f32(f32_to_bf16_hw(hi[v]));
   }
 }
 
@@ -275,7 +326,7 @@ __device__ __forceinline__ void unpack8f(u32x4 r, float* f) {
 // with the weight on the input) + shared row + residual; residual_out =
 // bf16(acc); with gamma, out = acc * (1 / sqrt(mean(acc^2) + eps)) * gamma;
 // bf16 out, or E4M3 with one scale per 128 columns.
-__device__ void finalize_token(const MonoArgs& a, int t, float* part) {
+__device__ void finalize_token(const MonoArgs& a, int t, int S, float* part) {
   constexpr int MAXC = 4;                   // H <= 16384
   const int tid = threadIdx.x;
   const int nch = a.H / 8;
@@ -292,13 +343,14 @@ __device__ void finalize_token(const MonoArgs& a, int t, float* part) {
         const int f = t * a.top_k + j;
         const float wj = a.woi ? 1.0f : a.wts[f];
         float yv[8];
-        unpack8f(ld16(a.y + static_cast<int64_t>(f) * a.H + c * 8), yv);
+        y8(a.yp + static_cast<int64_t>(f) * a.H + c * 8, static_cast<int64_t>(a.T) * a.top_k * a.H, S,
+           yv);
 #pragma unroll
         for (int v = 0; v < 8; ++v) acc[i][v] += wj * yv[v];
       }
       if (a.sw2) {
         float sv[8];
-        unpack8f(ld16(a.ysh + row + c * 8), sv);
+        y8(a.yshp + row + c * 8, static_cast<int64_t>(a.T) * a.H, S, sv);
 #pragma unroll
         for (int v = 0; v < 8; ++v) acc[i][v] += sv[v];
       }
@@ -394,7 +446,7 @@ __global__ __launch_bounds__(kMonoThreads) void moe_monolithic_kernel(MonoArgs a
   if (!grid_await(flags, go, a.epoch + 1, g, G_, &okf)) return;
 
   // B: first GEMMs
-  build_rows(a, tb);
+  build_rows(a, tb, nw);
   phase_gemm1<G>(a, tb, gw, nw);
   __syncthreads();
   grid_arrive(flags, a.epoch + 2, g);
@@ -407,7 +459,7 @@ __global__ __launch_bounds__(kMonoThreads) void moe_monolithic_kernel(MonoArgs a
   if (!grid_await(flags, go, a.epoch + 3, g, G_, &okf)) return;
 
   // D: finalize
-  for (int t = g; t < a.T; t += G_) finalize_token(a, t, part);
+  for (int t = g; t < a.T; t += G_) finalize_token(a, t, tb.ksplit, part);
 }
 
 template <int VPL>
@@ -427,8 +479,8 @@ bool monolithic_fits(int T, int top_k) {
 size_t monolithic_workspace_bytes(int T, int H, int top_k, int I, int Is) {
   const size_t n = static_cast<size_t>(T) * top_k;
   return align_up((kMonoMaxGrid + 1) * sizeof(uint64_t)) + align_up(n * 4) * 2 +
-         align_up(n * I * 2) + align_up(static_cast<size_t>(T) * Is * 2) + align_up(n * H * 2) +
-         align_up(static_cast<size_t>(T) * H * 2);
+         align_up(n * I * 2) + align_up(static_cast<size_t>(T) * Is * 2) +
+         align_up(kMonoMaxSplit * n * H * 4) + align_up(static_cast<size_t>(kMonoMaxSplit) * T * H * 4);
 }
 
 // Workgroups the launch may use: one per CU of the stream's CU mask (the
@@ -493,9 +545,9 @@ int launch_monolithic(const MonoLaunch& m, hipStream_t s) {
   p += align_up(n * m.I * 2);
   a.zsh = reinterpret_cast<uint16_t*>(p);
   p += align_up(static_cast<size_t>(m.T) * m.Is * 2);
-  a.y = reinterpret_cast<uint16_t*>(p);
-  p += align_up(n * m.H * 2);
-  a.ysh = reinterpret_cast<uint16_t*>(p);
+  a.yp = reinterpret_cast<float*>(p);
+  p += align_up(kMonoMaxSplit * n * m.H * 4);
+  a.yshp = reinterpret_cast<float*>(p);
   a.epoch = next_epoch() & ~static_cast<uint64_t>(3);
   if (m.E <= 64) launch_vpl<1>(a, grid, s);
   else if (m.E <= 128) launch_vpl<2>(a, grid, s);
