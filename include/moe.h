@@ -362,9 +362,10 @@ size_t moe_forward_workspace_bytes(int T, int H, int top_k, const moe_weights* w
                                    int activation, int block_m,
                                    int apply_router_weight_on_input);
 /*
- * moe_forward_graph_* -- the whole layer as one launch ("[vLLM] MoE Oracle &
- * Prepare/Finalize", modular vs monolithic: the monolithic mode runs the
- * layer fused into a single launch).  create captures moe_forward, for
+ * moe_forward_graph_* -- the modular layer submitted as one graph launch (the
+ * kernels of moe_forward; the fused single kernel of "[vLLM] MoE Oracle &
+ * Prepare/Finalize"'s monolithic mode is moe_forward_monolithic below).
+ * create captures moe_forward, for
  * exactly these sizes, weights and buffers, into an executable HIP graph;
  * launch replays it on any stream with one call, with no per-kernel host
  * work -- what a decode step needs, where the layer's kernels are shorter

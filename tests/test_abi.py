@@ -227,3 +227,31 @@ def test_graph_entry_validation(moe):
     assert not h.value
     assert L.moe_forward_graph_destroy(None) == 0
     assert L.moe_forward_graph_launch(None, None) == 1
+
+
+def test_one_launch_entry_validation(moe):
+    """moe_forward_monolithic refuses, before any HIP call, what its one
+    kernel does not cover: fp8 weights, more than 64 routed rows or 64
+    tokens, a missing or short workspace (status 2 = UNSUPPORTED, 3 =
+    WORKSPACE); its workspace grows with the rows and hidden size."""
+    L = moe.binding.lib()
+    fake = ctypes.c_void_p(256)           # never dereferenced on these paths
+    w = moe.MoeWeights()
+    w.num_experts, w.inter, w.quant, w.shared_inter = 8, 128, 0, 0
+    w.w13 = w.w2 = fake
+
+    def call(T, k, weights, ws=None, wsb=0):
+        return L.moe_forward_monolithic(fake, fake, T, 128, k, 0, 1, 0, ctypes.byref(weights), 0,
+                                        None, None, 1e-6, 0, fake, None, None, ws, wsb, None)
+    assert call(0, 2, w) == 0                      # no tokens: nothing to do
+    assert call(33, 2, w) == 2                     # 66 rows
+    assert call(65, 1, w) == 2                     # 65 tokens
+    assert call(4, 2, w) == 3                      # no workspace
+    need = L.moe_forward_monolithic_workspace_bytes(4, 128, 2, ctypes.byref(w), 0)
+    assert call(4, 2, w, fake, need - 1) == 3
+    assert need < L.moe_forward_monolithic_workspace_bytes(8, 128, 2, ctypes.byref(w), 0)
+    assert need < L.moe_forward_monolithic_workspace_bytes(4, 256, 2, ctypes.byref(w), 0)
+    f = moe.MoeWeights()
+    f.num_experts, f.inter, f.quant, f.shared_inter = 8, 128, moe.binding.QUANT["fp8"], 0
+    f.w13 = f.w2 = f.w13_scale = f.w2_scale = fake
+    assert call(4, 2, f) == 2
