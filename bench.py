@@ -469,6 +469,9 @@ def main():
         "graph": None if res["graph_ms"] is None else {
             "ms_per_step": round(res["graph_ms"], 4),
             "tokens_per_s": round(spec.T / (res["graph_ms"] * 1e-3), 1)},
+        "one_launch": None if res["mono_ms"] is None else {
+            "ms_per_step": round(res["mono_ms"], 4),
+            "tokens_per_s": round(spec.T / (res["mono_ms"] * 1e-3), 1)},
         "wall_s": round(res["wall"], 3),
         "roofline": _roofline(spec, res, traffic),
     }
