@@ -402,8 +402,8 @@ int moe_forward_graph_destroy(moe_graph* graph);
  * barriers between the phases, so its workgroups must all be resident at
  * once: one per CU the stream may use.
  *   Arguments as moe_forward (no block_m, no stage events), with these
- *   limits: bf16 weights (quant MOE_QUANT_NONE), 1 <= T <= 64,
- *   T*top_k <= 64; out_quant MOE_QUANT_NONE or MOE_QUANT_FP8_G128.
+ *   limits: bf16 weights (quant MOE_QUANT_NONE), 1 <= T <= 512,
+ *   T*top_k <= 512; out_quant MOE_QUANT_NONE or MOE_QUANT_FP8_G128.
  *   workspace (device): at least moe_forward_monolithic_workspace_bytes.
  *   The result equals moe_forward's up to the summation order of the GEMMs
  *   (fp32 sums of the same bf16 products, rounded once to bf16).

@@ -387,8 +387,8 @@ def moe_forward_monolithic(x, logits, weights, top_k, scoring="softmax", renorma
                            apply_router_weight_on_input=False, activation="silu", residual=None,
                            gamma=None, eps=1e-6, out_quant="none", output=None, output_scale=None,
                            residual_out=None, workspace=None, stream=None):
-    """The whole layer as one kernel launch (bf16 weights, T <= 64,
-    T*top_k <= 64); arguments and results as moe_forward."""
+    """The whole layer as one kernel launch (bf16 weights, T <= 512,
+    T*top_k <= 512); arguments and results as moe_forward."""
     T, H = x.shape
     dev = x.device
     if output is None:

@@ -1065,7 +1065,7 @@ int moe_forward_monolithic(const uint16_t* x, const float* logits, int T, int H,
   if (weights->quant != MOE_QUANT_NONE)
     return fail(MOE_ERR_UNSUPPORTED, "the one-launch layer takes bf16 weights only");
   if (!moe::monolithic_fits(T, top_k))
-    return fail(MOE_ERR_UNSUPPORTED, "the one-launch layer needs T <= 64 and T*top_k <= 64 (T=%d, top_k=%d)",
+    return fail(MOE_ERR_UNSUPPORTED, "the one-launch layer needs T <= 512 and T*top_k <= 512 (T=%d, top_k=%d)",
                 T, top_k);
   const size_t need = moe_forward_monolithic_workspace_bytes(T, H, top_k, weights, activation);
   if (!workspace || workspace_bytes < need)

@@ -7,8 +7,8 @@
 
 namespace moe {
 
-// The whole layer in one launch (monolithic.hip): bf16 weights, T <= 64,
-// T*top_k <= 64.  Pointers as moe_forward's; ws holds
+// The whole layer in one launch (monolithic.hip): bf16 weights, T <= 512,
+// T*top_k <= 512.  Pointers as moe_forward's; ws holds
 // monolithic_workspace_bytes.  Returns -1 (nothing launched) when the kernel
 // cannot have one workgroup resident on every CU of the stream.
 struct MonoLaunch {

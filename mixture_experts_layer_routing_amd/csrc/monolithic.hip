@@ -1,7 +1,7 @@
 // The whole layer in one launch for decode-sized batches: the monolithic
 // mode of "[vLLM] MoE Oracle & Prepare/Finalize" (section on modular vs
 // monolithic kernels: the monolithic mode fuses routing, the experts and
-// finalize into a single kernel), for bf16 weights, T <= 64 and T*top_k <= 64.
+// finalize into a single kernel), for bf16 weights, T <= 512 and T*top_k <= 512.
 //
 // One persistent launch, one 512-thread workgroup per CU the stream may use
 // (all resident at once), four phases with a grid barrier between each two
@@ -39,7 +39,8 @@ namespace moe {
 namespace {
 
 constexpr int kMonoThreads = 512, kMonoWaves = kMonoThreads / 64;
-constexpr int kMonoMaxRows = 64;      // T * top_k
+constexpr int kMonoMaxRows = 512;     // T * top_k (and T)
+constexpr int kMonoMaxGroups = kMonoMaxRows + kMonoMaxRows / 16;   // 16-row groups, routed
 constexpr int kMonoMaxGrid = kMonoThreads;   // arrival flags (workgroup 0 polls one a thread)
 constexpr int kMonoMaxSplit = 8;     // K split of the second GEMMs
 
@@ -69,6 +70,7 @@ struct MonoArgs {
   float* yshp;            // [S][T][H]
   uint64_t* flags;        // [kMonoMaxGrid] arrival flags, then the go word
   uint64_t epoch;
+  int max_split;          // bound on the second GEMMs' K split (the workspace's partials)
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -147,153 +149,200 @@ __device__ __forceinline__ void wave_gemm_k(const uint16_t* arow, float aw,
   else wave_gemm<G, 2, WOI>(arow, aw, wrow, k0, K, q, acc);
 }
 
-// The routed rows sorted by expert (LDS, built by wave 0): rows[p] is the
-// p-th flat row t*top_k+j in expert order, flat order within an expert;
-// expert s of the touched ones is slot_e[s], its rows rows[slot_off[s] ..
-// slot_off[s+1]).
+// The routed rows sorted by expert (LDS): rows[p] is the p-th flat row
+// t*top_k+j in expert order, flat order within an expert; the touched
+// experts' rows cut into groups of up to 16 (a group never spans two
+// experts): group g < n_groups belongs to expert slot_e[grp_slot[g]] and
+// holds rows rows[grp_row0[g] .. grp_row1[g]).  The shared expert's groups
+// follow (tokens 16 j ..), n_sgroups of them.
 struct RowTable {
+  int ids[kMonoMaxRows];
   int rows[kMonoMaxRows];
   int slot_e[kMonoMaxRows];
   int slot_off[kMonoMaxRows + 1];
-  int ids[kMonoMaxRows];
-  int n_slots;
+  int grp_slot[kMonoMaxGroups];
+  int grp_row0[kMonoMaxGroups];
+  int grp_row1[kMonoMaxGroups];
+  int wsum[kMonoWaves];
+  int n_slots, n_groups, n_sgroups;
   int ksplit;           // the second GEMMs' K split (see phase_gemm2)
 };
 
-__device__ void build_rows(const MonoArgs& a, RowTable& tb, int nw) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int n = a.T * a.top_k;
-  if (tid < 64) tb.ids[lane] = lane < n ? a.ids[lane] : 0x7fffffff;
+// Exclusive prefix sum of v over the workgroup's threads (thread order);
+// *total gets the sum.  Every thread calls it.
+__device__ int block_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  if (tid < 64) {
-    const int my = tb.ids[lane];
-    int less = 0, before = 0;
-    for (int j = 0; j < n; ++j) {
-      const int o = tb.ids[j];
-      less += o < my;
-      before += (o == my) & (j < lane);
-    }
-    if (lane < n) tb.rows[less + before] = lane;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kMonoWaves; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    all += wsum[w];
   }
   __syncthreads();
-  if (tid < 64) {
-    const int e = lane < n ? tb.ids[tb.rows[lane]] : -1;
-    const int prev = (lane > 0 && lane < n) ? tb.ids[tb.rows[lane - 1]] : -2;
-    const bool first = lane < n && e != prev;
-    const uint64_t m = __ballot(first);
-    const int slot = __builtin_popcountll(m & lanemask_lt());
-    if (first) {
-      tb.slot_e[slot] = e;
-      tb.slot_off[slot] = lane;
+  *total = all;
+  return before + x - v;
+}
+
+__device__ void build_rows(const MonoArgs& a, RowTable& tb, int nw) {
+  const int tid = threadIdx.x;
+  const int n = a.T * a.top_k;
+  static_assert(kMonoThreads >= kMonoMaxRows, "a thread per routed row");
+  if (tid < n) tb.ids[tid] = a.ids[tid];
+  __syncthreads();
+  // row tid's place: rows of smaller experts, then earlier rows of its own
+  if (tid < n) {
+    const int my = tb.ids[tid];
+    int pos = 0;
+    for (int j = 0; j < n; ++j) {
+      const int o = tb.ids[j];
+      pos += (o < my) | ((o == my) & (j < tid));
     }
-    if (lane == 0) {
-      const int ns = __builtin_popcountll(m);
-      tb.n_slots = ns;
-      tb.slot_off[ns] = n;
-      // Second GEMMs: split K in S (a power of two up to 8) while the items
-      // still fit the waves and every slice stays whole 64-deep batches --
-      // at T = 1 the H/16 column items of one or two experts leave most
-      // waves idle otherwise.
-      const int items = (ns + (a.sw2 ? 1 : 0)) * (a.H / 16);
-      int S = 1;
-      while (S < kMonoMaxSplit && items * S * 2 <= nw && a.I % (2 * S * 64) == 0 &&
-             (!a.sw2 || a.Is % (2 * S * 64) == 0))
-        S *= 2;
-      tb.ksplit = S;
+    tb.rows[pos] = tid;
+  }
+  __syncthreads();
+  // touched experts: a slot where the expert changes along rows[]
+  int e = -1;
+  bool first = false;
+  if (tid < n) {
+    e = tb.ids[tb.rows[tid]];
+    first = tid == 0 || e != tb.ids[tb.rows[tid - 1]];
+  }
+  int ns = 0;
+  const int slot = block_scan(first ? 1 : 0, tb.wsum, &ns);
+  if (first) {
+    tb.slot_e[slot] = e;
+    tb.slot_off[slot] = tid;
+  }
+  if (tid == 0) tb.slot_off[ns] = n;
+  __syncthreads();
+  // 16-row groups of each slot
+  int ng = 0;
+  if (tid < ns) ng = (tb.slot_off[tid + 1] - tb.slot_off[tid] + 15) / 16;
+  int total = 0;
+  const int g0 = block_scan(ng, tb.wsum, &total);
+  if (tid < ns)
+    for (int j = 0; j < ng; ++j) {
+      tb.grp_slot[g0 + j] = tid;
+      tb.grp_row0[g0 + j] = tb.slot_off[tid] + 16 * j;
+      tb.grp_row1[g0 + j] = min(tb.slot_off[tid] + 16 * j + 16, tb.slot_off[tid + 1]);
     }
+  if (tid == 0) {
+    tb.n_slots = ns;
+    tb.n_groups = total;
+    tb.n_sgroups = a.sw13 ? (a.T + 15) / 16 : 0;
+    // Second GEMMs: split K in S (a power of two up to a.max_split) while the
+    // items still fit the waves twice over and every slice stays whole 64-deep
+    // batches -- at T = 1 the H/16 column items of one or two experts leave
+    // most waves idle otherwise.
+    const int items = (total + tb.n_sgroups) * (a.H / 16);
+    int S = 1;
+    while (S < a.max_split && items * S * 2 <= nw && a.I % (2 * S * 64) == 0 &&
+           (!a.sw2 || a.Is % (2 * S * 64) == 0))
+      S *= 2;
+    tb.ksplit = S;
   }
   __syncthreads();
 }
 
-// Phase B: first GEMMs.  Item i < n_slots * I/16: touched expert i / (I/16),
-// z columns 16 (i mod I/16) ..; then the shared expert's Is/16 items.
+// Phase B: first GEMMs.  Item i < n_groups * I/16: routed row group
+// i / (I/16), z columns 16 (i mod I/16) ..; then the shared expert's row
+// groups times Is/16 columns.
 template <int G>
 __device__ void phase_gemm1(const MonoArgs& a, const RowTable& tb, int gw, int nw) {
   const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
   const int cw = a.I / 16, cs = a.Is / 16;
-  const int routed = tb.n_slots * cw;
-  const int total = routed + (a.sw13 ? cs : 0);
+  const int routed = tb.n_groups * cw;
+  const int total = routed + tb.n_sgroups * cs;
   for (int it = gw; it < total; it += nw) {
     const bool shared = it >= routed;
-    const int s = shared ? 0 : it / cw;
-    const int c = shared ? it - routed : it % cw;
+    const int j = shared ? it - routed : it;
+    const int grp = shared ? j / cs : j / cw;
+    const int c = shared ? j % cs : j % cw;
     const int In = shared ? a.Is : a.I;
     const uint16_t* wb = shared ? a.sw13
-                                : a.w13 + static_cast<int64_t>(tb.slot_e[s]) * G * a.I * a.H;
+                                : a.w13 + static_cast<int64_t>(tb.slot_e[tb.grp_slot[grp]]) * G * a.I * a.H;
     const uint16_t* wrow[G];
     wrow[0] = wb + static_cast<int64_t>(16 * c + r16) * a.H;
     if constexpr (G == 2) wrow[1] = wb + static_cast<int64_t>(In + 16 * c + r16) * a.H;
-    const int nrows = shared ? a.T : tb.slot_off[s + 1] - tb.slot_off[s];
-    for (int r0 = 0; r0 < nrows; r0 += 16) {
-      const int rr = r0 + r16;
-      int flat = -1, tok = -1;
-      if (rr < nrows) {
-        flat = shared ? rr : tb.rows[tb.slot_off[s] + rr];
-        tok = shared ? rr : flat / a.top_k;
-      }
-      const bool woi = a.woi && !shared;   // the shared expert reads the unweighted input
-      float aw = 1.0f;
-      if (woi && flat >= 0) aw = bf16_to_f32(f32_to_bf16(a.wts[flat]));
-      f32x4 acc[G];
+    // this lane's row of the group: a token (shared) or a flat routed row
+    int flat = -1, tok = -1;
+    if (shared) {
+      if (16 * grp + r16 < a.T) tok = flat = 16 * grp + r16;
+    } else if (tb.grp_row0[grp] + r16 < tb.grp_row1[grp]) {
+      flat = tb.rows[tb.grp_row0[grp] + r16];
+      tok = flat / a.top_k;
+    }
+    const bool woi = a.woi && !shared;   // the shared expert reads the unweighted input
+    float aw = 1.0f;
+    if (woi && flat >= 0) aw = bf16_to_f32(f32_to_bf16(a.wts[flat]));
+    f32x4 acc[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // (lanes without a row read token 0; their column is not stored)
-      const uint16_t* arow = a.x + static_cast<int64_t>(tok >= 0 ? tok : 0) * a.H;
-      if (woi) wave_gemm_k<G, true>(arow, aw, wrow, 0, a.H, q, acc);
-      else wave_gemm_k<G, false>(arow, aw, wrow, 0, a.H, q, acc);
-      if (rr < nrows) {
-        uint16_t* zr = (shared ? a.zsh + static_cast<int64_t>(rr) * a.Is
-                               : a.z + static_cast<int64_t>(flat) * a.I) + 16 * c + 4 * q;
-        float zv[4];
+    for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // (lanes without a row read token 0; their column is not stored)
+    const uint16_t* arow = a.x + static_cast<int64_t>(tok >= 0 ? tok : 0) * a.H;
+    if (woi) wave_gemm_k<G, true>(arow, aw, wrow, 0, a.H, q, acc);
+    else wave_gemm_k<G, false>(arow, aw, wrow, 0, a.H, q, acc);
+    if (flat >= 0) {
+      uint16_t* zr = (shared ? a.zsh + static_cast<int64_t>(flat) * a.Is
+                             : a.z + static_cast<int64_t>(flat) * a.I) + 16 * c + 4 * q;
+      float zv[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          zv[v] = G == 2 ? act_apply(a.act, acc[0][v]) * acc[G - 1][v] : act_apply(a.act, acc[0][v]);
-        u32x2 pk;
-        pk[0] = f32_to_bf16_hw(zv[0]) | (f32_to_bf16_hw(zv[1]) << 16);
-        pk[1] = f32_to_bf16_hw(zv[2]) | (f32_to_bf16_hw(zv[3]) << 16);
-        *reinterpret_cast<u32x2*>(zr) = pk;
-      }
+      for (int v = 0; v < 4; ++v)
+        zv[v] = G == 2 ? act_apply(a.act, acc[0][v]) * acc[G - 1][v] : act_apply(a.act, acc[0][v]);
+      u32x2 pk;
+      pk[0] = f32_to_bf16_hw(zv[0]) | (f32_to_bf16_hw(zv[1]) << 16);
+      pk[1] = f32_to_bf16_hw(zv[2]) | (f32_to_bf16_hw(zv[3]) << 16);
+      *reinterpret_cast<u32x2*>(zr) = pk;
     }
   }
 }
 
 // Phase C: second GEMMs in fp32 partials over S slices of K (S =
-// tb.ksplit).  Item i < n_slots * H/16 * S: slice i mod S of touched expert
-// (i / S) / (H/16), H columns 16 ((i / S) mod H/16) ..; then the shared
-// expert's H/16 * S items.  Finalize sums the slices in order and rounds once
-// to bf16, the value of an unsplit sum up to its order.
+// tb.ksplit).  Item i < n_groups * H/16 * S: slice i mod S of routed row
+// group (i / S) / (H/16), H columns 16 ((i / S) mod H/16) ..; then the
+// shared expert's groups likewise.  Finalize sums the slices in order and
+// rounds once to bf16, the value of an unsplit sum up to its order.
 __device__ void phase_gemm2(const MonoArgs& a, const RowTable& tb, int gw, int nw) {
   const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
   const int ch = a.H / 16, S = tb.ksplit;
   const int n = a.T * a.top_k;
-  const int routed = tb.n_slots * ch * S;
-  const int total = routed + (a.sw2 ? ch * S : 0);
+  const int routed = tb.n_groups * ch * S;
+  const int total = routed + tb.n_sgroups * ch * S;
   for (int it = gw; it < total; it += nw) {
     const bool shared = it >= routed;
     const int j = shared ? it - routed : it;
     const int sp = j % S, rest = j / S;
-    const int s = shared ? 0 : rest / ch;
-    const int c = shared ? rest : rest % ch;
+    const int grp = rest / ch, c = rest % ch;
     const int K = shared ? a.Is : a.I;
     const int Ks = K / S;
-    const uint16_t* wb = shared ? a.sw2 : a.w2 + static_cast<int64_t>(tb.slot_e[s]) * a.H * a.I;
+    const uint16_t* wb = shared ? a.sw2
+                                : a.w2 + static_cast<int64_t>(tb.slot_e[tb.grp_slot[grp]]) * a.H * a.I;
     const uint16_t* wrow[1] = {wb + static_cast<int64_t>(16 * c + r16) * K};
-    const int nrows = shared ? a.T : tb.slot_off[s + 1] - tb.slot_off[s];
-    for (int r0 = 0; r0 < nrows; r0 += 16) {
-      const int rr = r0 + r16;
-      int flat = -1;
-      if (rr < nrows) flat = shared ? rr : tb.rows[tb.slot_off[s] + rr];
-      // (lanes without a row read the group's first row; not stored)
-      const int src = flat >= 0 ? flat : (shared ? 0 : tb.rows[tb.slot_off[s]]);
-      const uint16_t* arow = shared ? a.zsh + static_cast<int64_t>(src) * a.Is
-                                    : a.z + static_cast<int64_t>(src) * a.I;
-      f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-      wave_gemm_k<1, false>(arow, 1.0f, wrow, sp * Ks, Ks, q, acc);
-      if (flat >= 0) {
-        float* yr = shared ? a.yshp + (static_cast<int64_t>(sp) * a.T + flat) * a.H
-                           : a.yp + (static_cast<int64_t>(sp) * n + flat) * a.H;
-        *reinterpret_cast<f32x4*>(yr + 16 * c + 4 * q) = acc[0];
-      }
+    int flat = -1, src;
+    if (shared) {
+      if (16 * grp + r16 < a.T) flat = 16 * grp + r16;
+      src = flat >= 0 ? flat : 16 * grp;
+    } else {
+      if (tb.grp_row0[grp] + r16 < tb.grp_row1[grp]) flat = tb.rows[tb.grp_row0[grp] + r16];
+      src = flat >= 0 ? flat : tb.rows[tb.grp_row0[grp]];
+    }
+    // (lanes without a row read the group's first row; not stored)
+    const uint16_t* arow = shared ? a.zsh + static_cast<int64_t>(src) * a.Is
+                                  : a.z + static_cast<int64_t>(src) * a.I;
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    wave_gemm_k<1, false>(arow, 1.0f, wrow, sp * Ks, Ks, q, acc);
+    if (flat >= 0) {
+      float* yr = shared ? a.yshp + (static_cast<int64_t>(sp) * a.T + flat) * a.H
+                         : a.yp + (static_cast<int64_t>(sp) * n + flat) * a.H;
+      *reinterpret_cast<f32x4*>(yr + 16 * c + 4 * q) = acc[0];
     }
   }
 }
@@ -473,14 +522,25 @@ size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
 bool monolithic_fits(int T, int top_k) {
-  return T >= 1 && T <= 64 && static_cast<int64_t>(T) * top_k <= kMonoMaxRows;
+  return T >= 1 && T <= kMonoMaxRows && static_cast<int64_t>(T) * top_k <= kMonoMaxRows;
+}
+
+// The second GEMMs split K only while the items fit the waves twice over;
+// with at least H/16 items, and at most kMonoMaxGrid workgroups of
+// kMonoWaves waves, S stays below this bound.
+static int max_split(int H) {
+  const int items = std::max(H / 16, 1);
+  int S = 1;
+  while (S < kMonoMaxSplit && items * S * 2 <= kMonoMaxGrid * kMonoWaves) S *= 2;
+  return S;
 }
 
 size_t monolithic_workspace_bytes(int T, int H, int top_k, int I, int Is) {
   const size_t n = static_cast<size_t>(T) * top_k;
+  const size_t ms = static_cast<size_t>(max_split(H));
   return align_up((kMonoMaxGrid + 1) * sizeof(uint64_t)) + align_up(n * 4) * 2 +
          align_up(n * I * 2) + align_up(static_cast<size_t>(T) * Is * 2) +
-         align_up(kMonoMaxSplit * n * H * 4) + align_up(static_cast<size_t>(kMonoMaxSplit) * T * H * 4);
+         align_up(ms * n * H * 4) + align_up(ms * T * H * 4);
 }
 
 // Workgroups the launch may use: one per CU of the stream's CU mask (the
@@ -546,7 +606,8 @@ int launch_monolithic(const MonoLaunch& m, hipStream_t s) {
   a.zsh = reinterpret_cast<uint16_t*>(p);
   p += align_up(static_cast<size_t>(m.T) * m.Is * 2);
   a.yp = reinterpret_cast<float*>(p);
-  p += align_up(kMonoMaxSplit * n * m.H * 4);
+  a.max_split = max_split(m.H);
+  p += align_up(static_cast<size_t>(a.max_split) * n * m.H * 4);
   a.yshp = reinterpret_cast<float*>(p);
   a.epoch = next_epoch() & ~static_cast<uint64_t>(3);
   if (m.E <= 64) launch_vpl<1>(a, grid, s);

@@ -231,7 +231,7 @@ def test_graph_entry_validation(moe):
 
 def test_one_launch_entry_validation(moe):
     """moe_forward_monolithic refuses, before any HIP call, what its one
-    kernel does not cover: fp8 weights, more than 64 routed rows or 64
+    kernel does not cover: fp8 weights, more than 512 routed rows or 512
     tokens, a missing or short workspace (status 2 = UNSUPPORTED, 3 =
     WORKSPACE); its workspace grows with the rows and hidden size."""
     L = moe.binding.lib()
@@ -244,8 +244,8 @@ def test_one_launch_entry_validation(moe):
         return L.moe_forward_monolithic(fake, fake, T, 128, k, 0, 1, 0, ctypes.byref(weights), 0,
                                         None, None, 1e-6, 0, fake, None, None, ws, wsb, None)
     assert call(0, 2, w) == 0                      # no tokens: nothing to do
-    assert call(33, 2, w) == 2                     # 66 rows
-    assert call(65, 1, w) == 2                     # 65 tokens
+    assert call(257, 2, w) == 2                    # 514 rows
+    assert call(513, 1, w) == 2                    # 513 tokens
     assert call(4, 2, w) == 3                      # no workspace
     need = L.moe_forward_monolithic_workspace_bytes(4, 128, 2, ctypes.byref(w), 0)
     assert call(4, 2, w, fake, need - 1) == 3

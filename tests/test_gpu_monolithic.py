@@ -36,7 +36,7 @@ def _case(name, **kw):
     return dataclasses.replace(base, **kw)
 
 
-# bf16 weights, T <= 64, T*top_k <= 64
+# bf16 weights, T <= 512, T*top_k <= 512
 CASES = [
     _case("tiny"),                                                   # T=16, k=2
     _case("mixtral_mini", T=32),                                     # 64 rows over 8 experts
@@ -51,6 +51,11 @@ CASES = [
     _case("decode_split_mini"),                                      # H = I = 2048, shared
     _case("decode_split_no_mul_mini"),
     _case("shared_dense_mini", T=32),                                # 2 shared row groups
+    # up to 512 routed rows: experts with several 16-row groups, 16 shared groups
+    _case("llama4_mini"),                                            # T=157, top-1, weight on input
+    _case("mixtral_mini", T=200),                                    # 400 rows over 8 experts
+    _case("tiny", T=64, E=256, top_k=8, scoring="sigmoid"),          # 512 rows
+    _case("shared_dense_mini", T=256),                               # 512 rows, residual, RMSNorm
 ]
 
 
@@ -165,15 +170,42 @@ def test_monolithic_mixtral_full_size():
                         min_identical=0.9, allowance=allowance, maxnorm_slack=slack)
 
 
+def test_monolithic_llama4_full_size():
+    """Llama-4 at T=128 (H=5120, I=8192, E=16, top-1 with the weight on the
+    input, an 8192-wide shared expert): 64 sampled tokens against the
+    oracle."""
+    _announce("monolithic full llama4 T=128")
+    moe = _moe()
+    spec = CONFIGS["llama4"][0]
+    assert spec.T == 128
+    d = make_layer_inputs(spec, device=DEV)
+    w = _weights(moe, d)
+    out, scale = _run(moe, spec, d, w)
+    hw = {k: to_numpy_bits(d[k]) for k in WKEYS if d.get(k) is not None}
+    rng = np.random.default_rng(128)
+    tok = np.unique(np.concatenate([[0, spec.T - 1], rng.choice(spec.T, 62, replace=False)]))
+    refs = {mode: oracle.forward(to_numpy_bits(d["x"]), d["logits"].cpu().numpy(), hw, spec.top_k,
+                                 spec.scoring, spec.renormalize, 16,
+                                 spec.apply_router_weight_on_input, "none", spec.activation, mode,
+                                 tokens=tok)
+            for mode in ("exact", "mirrored")}
+    allowance, slack = output_allowance(spec, refs["mirrored"], d, hw)
+    got = f64_of_bf16(to_numpy_bits(out)[tok])
+    check_tolerance(got, _ref64(spec, refs["exact"]), _ref64(spec, refs["mirrored"]), "bf16",
+                    "monolithic llama4 T=128", min_identical=0.9, allowance=allowance,
+                    maxnorm_slack=slack)
+    del d, w
+
+
 def test_monolithic_rejects_what_it_does_not_cover():
     _announce("monolithic limits")
     moe = _moe()
     spec = _case("tiny")
     d = {k: v.to(DEV) for k, v in make_layer_inputs(spec).items()}
     w = _weights(moe, d)
-    # T * top_k above 64 rows
-    x = torch.zeros((40, spec.H), dtype=torch.bfloat16, device=DEV)
-    lg = torch.zeros((40, spec.E), dtype=torch.float32, device=DEV)
+    # T * top_k above 512 rows
+    x = torch.zeros((257, spec.H), dtype=torch.bfloat16, device=DEV)
+    lg = torch.zeros((257, spec.E), dtype=torch.float32, device=DEV)
     with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
         moe.moe_forward_monolithic(x, lg, w, spec.top_k)
     # fp8 weights
