@@ -360,9 +360,11 @@ def measure(a, torch, moe, spec, block_m=0, graph=True):
         g.close()
         del g
     # the one-launch layer (moe_forward_monolithic), where it applies: bf16
-    # weights, T <= 512, T*top_k <= 512
+    # weights, or fp8 with G(128) activations and no weight on the input;
+    # T <= 512, T*top_k <= 512
     mono_ms = None
-    if graph and spec.quant == "none" and spec.T <= 512 and spec.T * spec.top_k <= 512:
+    fits = spec.quant == "none" or (spec.quant == "fp8" and not spec.apply_router_weight_on_input)
+    if graph and fits and spec.T <= 512 and spec.T * spec.top_k <= 512:
         def mono(out_m=None, ws_m=None):
             return moe.moe_forward_monolithic(
                 d["x"], d["logits"], w, spec.top_k, spec.scoring, spec.renormalize,

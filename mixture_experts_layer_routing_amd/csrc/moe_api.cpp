@@ -1047,7 +1047,8 @@ size_t moe_forward_monolithic_workspace_bytes(int T, int H, int top_k, const moe
   if (!weights || T <= 0 || top_k <= 0 || H <= 0) return 0;
   (void)activation;
   return moe::monolithic_workspace_bytes(T, H, top_k, weights->inter,
-                                         std::max(weights->shared_inter, 0));
+                                         std::max(weights->shared_inter, 0),
+                                         quant_fp8(weights->quant));
 }
 
 int moe_forward_monolithic(const uint16_t* x, const float* logits, int T, int H, int top_k,
@@ -1062,8 +1063,11 @@ int moe_forward_monolithic(const uint16_t* x, const float* logits, int T, int H,
                             weights, activation, 0, eps, out_quant, output, output_scale, &bm))
     return st;
   if (T == 0) return MOE_OK;
-  if (weights->quant != MOE_QUANT_NONE)
-    return fail(MOE_ERR_UNSUPPORTED, "the one-launch layer takes bf16 weights only");
+  if (weights->quant != MOE_QUANT_NONE && weights->quant != MOE_QUANT_FP8_G128)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the one-launch layer takes bf16 weights or fp8 with G(128) activations");
+  if (weights->quant == MOE_QUANT_FP8_G128 && apply_router_weight_on_input)
+    return fail(MOE_ERR_UNSUPPORTED, "the one-launch layer's fp8 path has no weight on the input");
   if (!moe::monolithic_fits(T, top_k))
     return fail(MOE_ERR_UNSUPPORTED, "the one-launch layer needs T <= 512 and T*top_k <= 512 (T=%d, top_k=%d)",
                 T, top_k);
@@ -1095,6 +1099,11 @@ int moe_forward_monolithic(const uint16_t* x, const float* logits, int T, int H,
   m.sw13 = static_cast<const uint16_t*>(weights->shared_w13);
   m.sw2 = static_cast<const uint16_t*>(weights->shared_w2);
   m.Is = std::max(weights->shared_inter, 0);
+  m.fp8 = weights->quant == MOE_QUANT_FP8_G128 ? 1 : 0;
+  m.w13s = weights->w13_scale;
+  m.w2s = weights->w2_scale;
+  m.sw13s = weights->shared_w13_scale;
+  m.sw2s = weights->shared_w2_scale;
   m.residual = residual;
   m.gamma = gamma;
   m.eps = eps;

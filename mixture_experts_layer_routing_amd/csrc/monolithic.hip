@@ -34,6 +34,7 @@
 #include "grid_sync.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -47,13 +48,19 @@ constexpr int kMonoMaxSplit = 8;     // K split of the second GEMMs
 struct MonoArgs {
   const uint16_t* x;
   const float* logits;
-  int T, H, E, top_k, scoring, renorm, woi, act, gated;
-  const uint16_t* w13;    // [E][G*I][H]
+  int T, H, E, top_k, scoring, renorm, woi, act, gated, fp8;
+  const uint16_t* w13;    // [E][G*I][H]  (fp8: the same layout in bytes)
   const uint16_t* w2;     // [E][H][I]
   int I;
   const uint16_t* sw13;   // shared expert [G*Is][H], or null
   const uint16_t* sw2;    // [H][Is]
   int Is;
+  // fp8 weights: one fp32 scale per 128 x 128 block, [E][G*I/128][H/128],
+  // [E][H/128][I/128], and the shared expert's
+  const float* w13s;
+  const float* w2s;
+  const float* sw13s;
+  const float* sw2s;
   const uint16_t* residual;
   const uint16_t* gamma;
   float eps;
@@ -64,8 +71,16 @@ struct MonoArgs {
   // workspace
   int32_t* ids;           // [T*top_k]
   float* wts;             // [T*top_k]
-  uint16_t* z;            // [T*top_k][I]
+  uint16_t* z;            // [T*top_k][I] bf16 (fp8 weights: E4M3 codes, [T*top_k][I] bytes)
   uint16_t* zsh;          // [T][Is]
+  // fp8 weights: x as E4M3 G(128) codes and scales, z before its
+  // quantisation (fp32), and the scales of z
+  uint8_t* xq;            // [T][H]
+  float* xs;              // [T][H/128]
+  float* zf;              // [T*top_k][I]
+  float* zshf;            // [T][Is]
+  float* zs;              // [T*top_k][I/128]
+  float* zshs;            // [T][Is/128]
   float* yp;              // second-GEMM partials [S][T*top_k][H]
   float* yshp;            // [S][T][H]
   uint64_t* flags;        // [kMonoMaxGrid] arrival flags, then the go word
@@ -244,8 +259,9 @@ __device__ void build_rows(const MonoArgs& a, RowTable& tb, int nw) {
     // most waves idle otherwise.
     const int items = (total + tb.n_sgroups) * (a.H / 16);
     int S = 1;
-    while (S < a.max_split && items * S * 2 <= nw && a.I % (2 * S * 64) == 0 &&
-           (!a.sw2 || a.Is % (2 * S * 64) == 0))
+    const int kq = a.fp8 ? 128 : 64;     // slices of whole batches (fp8: k-tiles)
+    while (S < a.max_split && items * S * 2 <= nw && a.I % (2 * S * kq) == 0 &&
+           (!a.sw2 || a.Is % (2 * S * kq) == 0))
       S *= 2;
     tb.ksplit = S;
   }
@@ -468,7 +484,218 @@ __device__ void finalize_token(const MonoArgs& a, int t, int S, float* part) {
   }
 }
 
-template <int VPL, int G>
+// ---- fp8 weights ----------------------------------------------------------
+
+// Rows of width W (a multiple of 128) to E4M3 G(128) codes and one scale per
+// 128 columns, as prepare and the first GEMM's epilogue quantise: s =
+// max(amax, 1e-10) / 448, code = RNE(v / s).  Item = (row, 512 columns),
+// one wave each: lane l holds 8 columns, 16 lanes a 128-column group.
+template <class SRC>
+__device__ void quant_rows(const SRC* src, int rows, int W, uint8_t* q, float* sc, int gw, int nw) {
+  const int lane = threadIdx.x & 63;
+  const int per = (W + 511) / 512;
+  for (int it = gw; it < rows * per; it += nw) {
+    const int r = it / per, c0 = (it % per) * 512 + 8 * lane;
+    // lanes past the row (whole 16-lane groups: W % 128 == 0) take zeros
+    // through the group maximum and store nothing
+    const bool valid = c0 < W;
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (!valid) {
+    } else if constexpr (sizeof(SRC) == 2) {
+      const u32x4 v = ld16(reinterpret_cast<const uint16_t*>(src) + static_cast<int64_t>(r) * W + c0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(v[i]);
+        f[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+      }
+    } else {
+      const float* p = reinterpret_cast<const float*>(src) + static_cast<int64_t>(r) * W + c0;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(p), hi = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = lo[i];
+        f[4 + i] = hi[i];
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(f[i]));
+    amax = group_max<16>(amax);
+    const float s = fmaxf(amax, kQuantEps) / kFp8Max;
+    u32x2 o;
+    o[0] = pack4_e4m3(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
+    o[1] = pack4_e4m3(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
+    if (valid) {
+      *reinterpret_cast<u32x2*>(q + static_cast<int64_t>(r) * W + c0) = o;
+      if ((lane & 15) == 0) sc[static_cast<int64_t>(r) * (W / 128) + c0 / 128] = s;
+    }
+  }
+}
+
+// One wave, fp8: acc[g][v] += sum over k-tiles kt in [kt0, kt0 + nkt) of
+// (sum over the k-tile of a[row r16][k] * w_g[4q + v][k]) * sa[kt] * sw_g[kt]:
+// one 16x16x128 MFMA per k-tile and fragment from zero, promoted with the
+// row's activation scale and the fragment's weight-block scale (the 16 rows
+// lie in one 128-row block) -- the fp8 tiles' arithmetic.  Lane group q
+// holds bytes [32q, 32q+32) of each k-tile row.  One k-tile per batch, a
+// ring of four: three load while one feeds the MFMAs; every batch issues its
+// loads (clamped to the last k-tile) so the compiler's count stays exact.
+template <int G>
+__device__ __forceinline__ void wave_gemm_fp8(const uint8_t* arow, const float* asc,
+                                              const uint8_t* const (&wrow)[G],
+                                              const float* const (&wsc)[G], int kt0, int nkt, int q,
+                                              f32x4 (&acc)[G]) {
+  i32x8 A[4], W[4][G];
+  float SA[4], SW[4][G];
+  auto load = [&](int b, int buf) {
+    const int kt = kt0 + min(b, nkt - 1);
+    const int64_t k = static_cast<int64_t>(kt) * 128 + 32 * q;
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(arow + k);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(arow + k + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      A[buf][i] = a0[i];
+      A[buf][4 + i] = a1[i];
+    }
+    SA[buf] = asc[kt];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(wrow[g] + k);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(wrow[g] + k + 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        W[buf][g][i] = w0[i];
+        W[buf][g][4 + i] = w1[i];
+      }
+      SW[buf][g] = wsc[g][kt];
+    }
+  };
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  auto comp = [&](int buf) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(W[buf][g], A[buf], zero, 0, 0, 0,
+                                                                       0, 0, 0);
+      const float sc = SA[buf] * SW[buf][g];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[g][v] += p[v] * sc;
+    }
+  };
+  load(0, 0);
+  load(1, 1);
+  load(2, 2);
+  int b = 0;
+  for (; b + 4 <= nkt; b += 4) {
+    load(b + 3, 3);
+    comp(0);
+    load(b + 4, 0);
+    comp(1);
+    load(b + 5, 1);
+    comp(2);
+    load(b + 6, 2);
+    comp(3);
+  }
+  // the last nkt mod 4 k-tiles: b, b+1, b+2 in slots 0, 1, 2
+  if (b < nkt) comp(0);
+  if (b + 1 < nkt) comp(1);
+  if (b + 2 < nkt) comp(2);
+}
+
+// Phase B, fp8: as phase_gemm1, z = act(gate) * up in fp32 (quantised by
+// the next phase, which sees whole 128-column groups).
+template <int G>
+__device__ void phase_gemm1_fp8(const MonoArgs& a, const RowTable& tb, int gw, int nw) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
+  const int cw = a.I / 16, cs = a.Is / 16;
+  const int routed = tb.n_groups * cw;
+  const int total = routed + tb.n_sgroups * cs;
+  const int kb = a.H / 128;
+  for (int it = gw; it < total; it += nw) {
+    const bool shared = it >= routed;
+    const int j = shared ? it - routed : it;
+    const int grp = shared ? j / cs : j / cw;
+    const int c = shared ? j % cs : j % cw;
+    const int In = shared ? a.Is : a.I;
+    const int e = shared ? 0 : tb.slot_e[tb.grp_slot[grp]];
+    const uint8_t* wb = reinterpret_cast<const uint8_t*>(shared ? a.sw13 : a.w13) +
+                        static_cast<int64_t>(e) * G * a.I * a.H;
+    const float* sb = (shared ? a.sw13s : a.w13s) + static_cast<int64_t>(e) * (G * a.I / 128) * kb;
+    const uint8_t* wrow[G];
+    const float* wsc[G];
+    wrow[0] = wb + static_cast<int64_t>(16 * c + r16) * a.H;
+    wsc[0] = sb + static_cast<int64_t>((16 * c) / 128) * kb;
+    if constexpr (G == 2) {
+      wrow[1] = wb + static_cast<int64_t>(In + 16 * c + r16) * a.H;
+      wsc[1] = sb + static_cast<int64_t>((In + 16 * c) / 128) * kb;
+    }
+    int flat = -1, tok = -1;
+    if (shared) {
+      if (16 * grp + r16 < a.T) tok = flat = 16 * grp + r16;
+    } else if (tb.grp_row0[grp] + r16 < tb.grp_row1[grp]) {
+      flat = tb.rows[tb.grp_row0[grp] + r16];
+      tok = flat / a.top_k;
+    }
+    // (lanes without a row read token 0; their column is not stored)
+    const int t0 = tok >= 0 ? tok : 0;
+    f32x4 acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    wave_gemm_fp8<G>(a.xq + static_cast<int64_t>(t0) * a.H, a.xs + static_cast<int64_t>(t0) * kb,
+                     wrow, wsc, 0, kb, q, acc);
+    if (flat >= 0) {
+      float* zr = (shared ? a.zshf + static_cast<int64_t>(flat) * a.Is
+                          : a.zf + static_cast<int64_t>(flat) * a.I) + 16 * c + 4 * q;
+      f32x4 zv;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        zv[v] = G == 2 ? act_apply(a.act, acc[0][v]) * acc[G - 1][v] : act_apply(a.act, acc[0][v]);
+      *reinterpret_cast<f32x4*>(zr) = zv;
+    }
+  }
+}
+
+// Phase C, fp8: as phase_gemm2, on the E4M3 z rows and their scales.
+__device__ void phase_gemm2_fp8(const MonoArgs& a, const RowTable& tb, int gw, int nw) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
+  const int ch = a.H / 16, S = tb.ksplit;
+  const int n = a.T * a.top_k;
+  const int routed = tb.n_groups * ch * S;
+  const int total = routed + tb.n_sgroups * ch * S;
+  for (int it = gw; it < total; it += nw) {
+    const bool shared = it >= routed;
+    const int j = shared ? it - routed : it;
+    const int sp = j % S, rest = j / S;
+    const int grp = rest / ch, c = rest % ch;
+    const int K = shared ? a.Is : a.I;
+    const int kb = K / 128, nkt = kb / S;
+    const int e = shared ? 0 : tb.slot_e[tb.grp_slot[grp]];
+    const uint8_t* wb = reinterpret_cast<const uint8_t*>(shared ? a.sw2 : a.w2) +
+                        static_cast<int64_t>(e) * a.H * a.I;
+    const float* sb = (shared ? a.sw2s : a.w2s) + static_cast<int64_t>(e) * (a.H / 128) * (a.I / 128);
+    const uint8_t* wrow[1] = {wb + static_cast<int64_t>(16 * c + r16) * K};
+    const float* wsc[1] = {sb + static_cast<int64_t>((16 * c) / 128) * kb};
+    int flat = -1, src;
+    if (shared) {
+      if (16 * grp + r16 < a.T) flat = 16 * grp + r16;
+      src = flat >= 0 ? flat : 16 * grp;
+    } else {
+      if (tb.grp_row0[grp] + r16 < tb.grp_row1[grp]) flat = tb.rows[tb.grp_row0[grp] + r16];
+      src = flat >= 0 ? flat : tb.rows[tb.grp_row0[grp]];
+    }
+    const uint8_t* arow = reinterpret_cast<const uint8_t*>(shared ? a.zsh : a.z) +
+                          static_cast<int64_t>(src) * K;
+    const float* asc = (shared ? a.zshs : a.zs) + static_cast<int64_t>(src) * kb;
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    wave_gemm_fp8<1>(arow, asc, wrow, wsc, sp * nkt, nkt, q, acc);
+    if (flat >= 0) {
+      float* yr = shared ? a.yshp + (static_cast<int64_t>(sp) * a.T + flat) * a.H
+                         : a.yp + (static_cast<int64_t>(sp) * n + flat) * a.H;
+      *reinterpret_cast<f32x4*>(yr + 16 * c + 4 * q) = acc[0];
+    }
+  }
+}
+
+template <int VPL, int G, bool FP8>
 __global__ __launch_bounds__(kMonoThreads) void moe_monolithic_kernel(MonoArgs a) {
   __shared__ RowTable tb;
   __shared__ float part[kMonoWaves];
@@ -478,8 +705,15 @@ __global__ __launch_bounds__(kMonoThreads) void moe_monolithic_kernel(MonoArgs a
   const int gw = g * kMonoWaves + wave, nw = G_ * kMonoWaves;
   uint64_t* flags = a.flags;
   uint64_t* go = a.flags + kMonoMaxGrid;
+  uint64_t ep = a.epoch;
+  auto barrier = [&]() {
+    __syncthreads();
+    ++ep;
+    grid_arrive(flags, ep, g);
+    return grid_await(flags, go, ep, g, G_, &okf);
+  };
 
-  // A: routing, one wave per token
+  // A: routing, one wave per token (fp8: and x to E4M3 G(128))
   for (int t = gw; t < a.T; t += nw) {
     int e;
     float w;
@@ -490,31 +724,35 @@ __global__ __launch_bounds__(kMonoThreads) void moe_monolithic_kernel(MonoArgs a
       a.wts[t * a.top_k + lane] = w;
     }
   }
-  __syncthreads();
-  grid_arrive(flags, a.epoch + 1, g);
-  if (!grid_await(flags, go, a.epoch + 1, g, G_, &okf)) return;
+  if constexpr (FP8) quant_rows(a.x, a.T, a.H, a.xq, a.xs, gw, nw);
+  if (!barrier()) return;
 
   // B: first GEMMs
   build_rows(a, tb, nw);
-  phase_gemm1<G>(a, tb, gw, nw);
-  __syncthreads();
-  grid_arrive(flags, a.epoch + 2, g);
-  if (!grid_await(flags, go, a.epoch + 2, g, G_, &okf)) return;
+  if constexpr (FP8) {
+    phase_gemm1_fp8<G>(a, tb, gw, nw);
+    if (!barrier()) return;
+    // z to E4M3 G(128): the routed rows, then the shared expert's
+    quant_rows(a.zf, a.T * a.top_k, a.I, reinterpret_cast<uint8_t*>(a.z), a.zs, gw, nw);
+    if (a.sw13) quant_rows(a.zshf, a.T, a.Is, reinterpret_cast<uint8_t*>(a.zsh), a.zshs, gw, nw);
+  } else {
+    phase_gemm1<G>(a, tb, gw, nw);
+  }
+  if (!barrier()) return;
 
   // C: second GEMMs
-  phase_gemm2(a, tb, gw, nw);
-  __syncthreads();
-  grid_arrive(flags, a.epoch + 3, g);
-  if (!grid_await(flags, go, a.epoch + 3, g, G_, &okf)) return;
+  if constexpr (FP8) phase_gemm2_fp8(a, tb, gw, nw);
+  else phase_gemm2(a, tb, gw, nw);
+  if (!barrier()) return;
 
   // D: finalize
   for (int t = g; t < a.T; t += G_) finalize_token(a, t, tb.ksplit, part);
 }
 
-template <int VPL>
+template <int VPL, bool FP8>
 void launch_vpl(const MonoArgs& a, int grid, hipStream_t s) {
-  if (a.gated) moe_monolithic_kernel<VPL, 2><<<grid, kMonoThreads, 0, s>>>(a);
-  else moe_monolithic_kernel<VPL, 1><<<grid, kMonoThreads, 0, s>>>(a);
+  if (a.gated) moe_monolithic_kernel<VPL, 2, FP8><<<grid, kMonoThreads, 0, s>>>(a);
+  else moe_monolithic_kernel<VPL, 1, FP8><<<grid, kMonoThreads, 0, s>>>(a);
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -535,22 +773,52 @@ static int max_split(int H) {
   return S;
 }
 
-size_t monolithic_workspace_bytes(int T, int H, int top_k, int I, int Is) {
-  const size_t n = static_cast<size_t>(T) * top_k;
+// Workspace: arrival flags, go word and spare words; ids and weights; z of
+// the routed rows and of the shared expert (bf16, or E4M3 bytes in the same
+// room); the second GEMMs' fp32 partials; with fp8 weights also x's codes
+// and scales, fp32 z before its quantisation, and z's scales.
+struct MonoLayout {
+  size_t flags, ids, wts, z, zsh, yp, yshp, xq, xs, zf, zshf, zs, zshs, bytes;
+};
+
+MonoLayout mono_layout(int T, int H, int top_k, int I, int Is, bool fp8) {
+  const size_t n = static_cast<size_t>(T) * top_k, t = static_cast<size_t>(T);
   const size_t ms = static_cast<size_t>(max_split(H));
-  return align_up((kMonoMaxGrid + 1) * sizeof(uint64_t)) + align_up(n * 4) * 2 +
-         align_up(n * I * 2) + align_up(static_cast<size_t>(T) * Is * 2) +
-         align_up(ms * n * H * 4) + align_up(ms * T * H * 4);
+  MonoLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
+  L.flags = take((kMonoMaxGrid + 3) * sizeof(uint64_t));
+  L.ids = take(n * 4);
+  L.wts = take(n * 4);
+  L.z = take(n * I * 2);
+  L.zsh = take(t * Is * 2);
+  L.yp = take(ms * n * H * 4);
+  L.yshp = take(ms * t * H * 4);
+  if (fp8) {
+    L.xq = take(t * H);
+    L.xs = take(t * (H / 128) * 4);
+    L.zf = take(n * I * 4);
+    L.zshf = take(t * Is * 4);
+    L.zs = take(n * (I / 128) * 4);
+    L.zshs = take(t * (Is / 128) * 4);
+  }
+  L.bytes = o;
+  return L;
+}
+
+size_t monolithic_workspace_bytes(int T, int H, int top_k, int I, int Is, bool fp8) {
+  return mono_layout(T, H, top_k, I, Is, fp8).bytes;
 }
 
 // Workgroups the launch may use: one per CU of the stream's CU mask (the
 // kernel fits a CU), 0 if it does not fit at all.
-int monolithic_grid(hipStream_t s) {
+int monolithic_grid(hipStream_t s, bool fp8, bool gated) {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, moe_monolithic_kernel<16, 2>, kMonoThreads,
-                                                   0) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, moe_monolithic_kernel<16, 1>, kMonoThreads,
-                                                   0) != hipSuccess) {
+  const void* k = fp8 ? (gated ? reinterpret_cast<const void*>(moe_monolithic_kernel<16, 2, true>)
+                               : reinterpret_cast<const void*>(moe_monolithic_kernel<16, 1, true>))
+                      : (gated ? reinterpret_cast<const void*>(moe_monolithic_kernel<16, 2, false>)
+                               : reinterpret_cast<const void*>(moe_monolithic_kernel<16, 1, false>));
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, kMonoThreads, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -561,12 +829,12 @@ int monolithic_grid(hipStream_t s) {
     return 0;
   }
   int cus = 0;
-  for (uint32_t m : mask) cus += __builtin_popcount(m);
+  for (uint32_t mk : mask) cus += __builtin_popcount(mk);
   return std::min(cus, kMonoMaxGrid);
 }
 
 int launch_monolithic(const MonoLaunch& m, hipStream_t s) {
-  const int grid = monolithic_grid(s);
+  const int grid = monolithic_grid(s, m.fp8 != 0, m.gated != 0);
   if (grid <= 0) return -1;
   MonoArgs a{};
   a.x = m.x;
@@ -580,12 +848,17 @@ int launch_monolithic(const MonoLaunch& m, hipStream_t s) {
   a.woi = m.woi;
   a.act = m.act;
   a.gated = m.gated;
+  a.fp8 = m.fp8;
   a.w13 = m.w13;
   a.w2 = m.w2;
   a.I = m.I;
   a.sw13 = m.Is > 0 ? m.sw13 : nullptr;
   a.sw2 = m.Is > 0 ? m.sw2 : nullptr;
   a.Is = m.Is;
+  a.w13s = m.w13s;
+  a.w2s = m.w2s;
+  a.sw13s = m.Is > 0 ? m.sw13s : nullptr;
+  a.sw2s = m.Is > 0 ? m.sw2s : nullptr;
   a.residual = m.residual;
   a.gamma = m.gamma;
   a.eps = m.eps;
@@ -593,28 +866,36 @@ int launch_monolithic(const MonoLaunch& m, hipStream_t s) {
   a.out = m.out;
   a.out_scale = m.out_scale;
   a.residual_out = m.residual_out;
-  const size_t n = static_cast<size_t>(m.T) * m.top_k;
+  const MonoLayout L = mono_layout(m.T, m.H, m.top_k, m.I, m.Is, m.fp8 != 0);
   uint8_t* p = static_cast<uint8_t*>(m.ws);
-  a.flags = reinterpret_cast<uint64_t*>(p);
-  p += align_up((kMonoMaxGrid + 1) * sizeof(uint64_t));
-  a.ids = reinterpret_cast<int32_t*>(p);
-  p += align_up(n * 4);
-  a.wts = reinterpret_cast<float*>(p);
-  p += align_up(n * 4);
-  a.z = reinterpret_cast<uint16_t*>(p);
-  p += align_up(n * m.I * 2);
-  a.zsh = reinterpret_cast<uint16_t*>(p);
-  p += align_up(static_cast<size_t>(m.T) * m.Is * 2);
-  a.yp = reinterpret_cast<float*>(p);
+  a.flags = reinterpret_cast<uint64_t*>(p + L.flags);
+  a.ids = reinterpret_cast<int32_t*>(p + L.ids);
+  a.wts = reinterpret_cast<float*>(p + L.wts);
+  a.z = reinterpret_cast<uint16_t*>(p + L.z);
+  a.zsh = reinterpret_cast<uint16_t*>(p + L.zsh);
+  a.yp = reinterpret_cast<float*>(p + L.yp);
+  a.yshp = reinterpret_cast<float*>(p + L.yshp);
+  if (m.fp8) {
+    a.xq = p + L.xq;
+    a.xs = reinterpret_cast<float*>(p + L.xs);
+    a.zf = reinterpret_cast<float*>(p + L.zf);
+    a.zshf = reinterpret_cast<float*>(p + L.zshf);
+    a.zs = reinterpret_cast<float*>(p + L.zs);
+    a.zshs = reinterpret_cast<float*>(p + L.zshs);
+  }
   a.max_split = max_split(m.H);
-  p += align_up(static_cast<size_t>(a.max_split) * n * m.H * 4);
-  a.yshp = reinterpret_cast<float*>(p);
-  a.epoch = next_epoch() & ~static_cast<uint64_t>(3);
-  if (m.E <= 64) launch_vpl<1>(a, grid, s);
-  else if (m.E <= 128) launch_vpl<2>(a, grid, s);
-  else if (m.E <= 256) launch_vpl<4>(a, grid, s);
-  else if (m.E <= 512) launch_vpl<8>(a, grid, s);
-  else launch_vpl<16>(a, grid, s);
+  // barriers take epoch + 1, + 2, ...: the low bits start at zero
+  a.epoch = next_epoch() & ~static_cast<uint64_t>(7);
+  auto go = [&](auto fp8) {
+    constexpr bool F = decltype(fp8)::value;
+    if (m.E <= 64) launch_vpl<1, F>(a, grid, s);
+    else if (m.E <= 128) launch_vpl<2, F>(a, grid, s);
+    else if (m.E <= 256) launch_vpl<4, F>(a, grid, s);
+    else if (m.E <= 512) launch_vpl<8, F>(a, grid, s);
+    else launch_vpl<16, F>(a, grid, s);
+  };
+  if (m.fp8) go(std::true_type{});
+  else go(std::false_type{});
   return 0;
 }
 

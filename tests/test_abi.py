@@ -231,9 +231,10 @@ def test_graph_entry_validation(moe):
 
 def test_one_launch_entry_validation(moe):
     """moe_forward_monolithic refuses, before any HIP call, what its one
-    kernel does not cover: fp8 weights, more than 512 routed rows or 512
-    tokens, a missing or short workspace (status 2 = UNSUPPORTED, 3 =
-    WORKSPACE); its workspace grows with the rows and hidden size."""
+    kernel does not cover: per-token or per-tensor fp8 activations, fp8 with
+    the weight on the input, more than 512 routed rows or 512 tokens, a
+    missing or short workspace (status 2 = UNSUPPORTED, 3 = WORKSPACE); its
+    workspace grows with the rows and hidden size, and with fp8."""
     L = moe.binding.lib()
     fake = ctypes.c_void_p(256)           # never dereferenced on these paths
     w = moe.MoeWeights()
@@ -252,6 +253,12 @@ def test_one_launch_entry_validation(moe):
     assert need < L.moe_forward_monolithic_workspace_bytes(8, 128, 2, ctypes.byref(w), 0)
     assert need < L.moe_forward_monolithic_workspace_bytes(4, 256, 2, ctypes.byref(w), 0)
     f = moe.MoeWeights()
-    f.num_experts, f.inter, f.quant, f.shared_inter = 8, 128, moe.binding.QUANT["fp8"], 0
+    f.num_experts, f.inter, f.quant, f.shared_inter = 8, 128, moe.binding.QUANT["fp8_token"], 0
     f.w13 = f.w2 = f.w13_scale = f.w2_scale = fake
-    assert call(4, 2, f) == 2
+    assert call(4, 2, f) == 2                      # per-token fp8 activations
+    f.quant = moe.binding.QUANT["fp8"]
+    assert call(4, 2, f) == 3                      # fp8 G(128): taken (no workspace here)
+    assert L.moe_forward_monolithic(fake, fake, 4, 128, 1, 0, 1, 1, ctypes.byref(f), 0, None,
+                                    None, 1e-6, 0, fake, None, None, None, 0, None) == 2
+    assert (L.moe_forward_monolithic_workspace_bytes(4, 128, 2, ctypes.byref(f), 0)
+            > L.moe_forward_monolithic_workspace_bytes(4, 128, 2, ctypes.byref(w), 0))

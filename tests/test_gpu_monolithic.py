@@ -19,7 +19,8 @@ from helpers import check_tolerance, output_allowance, f64_of_bf16, f64_of_fp8
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-WKEYS = ("w13", "w2", "shared_w13", "shared_w2")
+WKEYS = ("w13", "w2", "w13_scale", "w2_scale", "shared_w13", "shared_w2", "shared_w13_scale",
+         "shared_w2_scale")
 
 
 def _moe():
@@ -56,12 +57,19 @@ CASES = [
     _case("mixtral_mini", T=200),                                    # 400 rows over 8 experts
     _case("tiny", T=64, E=256, top_k=8, scoring="sigmoid"),          # 512 rows
     _case("shared_dense_mini", T=256),                               # 512 rows, residual, RMSNorm
+    # fp8 weights (E4M3, 128 x 128 blocks; x and z quantised to G(128) in the kernel)
+    _case("decode_split_fp8_mini"),                                  # T=3, k=4, shared, split K
+    _case("deepseek_mini", T=64),                                    # 512 rows, sigmoid, hot experts
+    _case("fp8_out_mini"),                                           # T=77, k=4, RMSNorm, fp8 out
+    _case("deepseek_mini", T=5, activation="silu_no_mul"),
 ]
 
 
-def _weights(moe, d):
-    return moe.make_weights(*(d.get(k) for k in ("w13", "w2", None, None, "shared_w13",
-                                                 "shared_w2", None, None)))
+def _weights(moe, d, quant="none"):
+    return moe.make_weights(*(d.get(k) for k in ("w13", "w2", "w13_scale", "w2_scale",
+                                                 "shared_w13", "shared_w2", "shared_w13_scale",
+                                                 "shared_w2_scale")),
+                            quant=None if quant == "none" else quant)
 
 
 def _run(moe, spec, dd, w):
@@ -89,14 +97,15 @@ def _check_against_oracle(spec, d, out, scale, label):
     hw = {k: to_numpy_bits(d[k]) for k in WKEYS if d.get(k) is not None}
     refs = {mode: oracle.forward(to_numpy_bits(d["x"]), d["logits"].cpu().numpy(), hw, spec.top_k,
                                  spec.scoring, spec.renormalize, 16,
-                                 spec.apply_router_weight_on_input, "none", spec.activation, mode,
-                                 to_numpy_bits(d.get("residual")), to_numpy_bits(d.get("gamma")),
-                                 spec.eps, spec.out_quant)
+                                 spec.apply_router_weight_on_input, spec.quant, spec.activation,
+                                 mode, to_numpy_bits(d.get("residual")),
+                                 to_numpy_bits(d.get("gamma")), spec.eps, spec.out_quant)
             for mode in ("exact", "mirrored")}
     allowance, slack = output_allowance(spec, refs["mirrored"], d, hw)
+    path = "fp8" if (spec.quant != "none" or spec.out_quant == "fp8") else "bf16"
     check_tolerance(_f64(spec, out, scale), _ref64(spec, refs["exact"]),
-                    _ref64(spec, refs["mirrored"]), "fp8" if spec.out_quant == "fp8" else "bf16",
-                    label, min_identical=0.9 if spec.out_quant != "fp8" else None,
+                    _ref64(spec, refs["mirrored"]), path, label,
+                    min_identical=0.9 if path == "bf16" else None,
                     allowance=allowance, maxnorm_slack=slack)
 
 
@@ -107,7 +116,7 @@ def test_monolithic_matches_the_oracle(spec):
     moe = _moe()
     d = make_layer_inputs(spec)
     dd = {k: v.to(DEV) for k, v in d.items()}
-    w = _weights(moe, dd)
+    w = _weights(moe, dd, spec.quant)
     out, scale = _run(moe, spec, dd, w)
     _check_against_oracle(spec, d, out, scale, f"monolithic {spec.name}")
     # a fixed summation order: a second launch gives the same bits
@@ -197,6 +206,34 @@ def test_monolithic_llama4_full_size():
     del d, w
 
 
+def test_monolithic_deepseek_full_size():
+    """DeepSeek-V3 fp8 at T=64 (H=7168, I=2048, E=256, top-8, a 2048-wide
+    shared expert): 512 routed rows over ~220 experts.  Four tokens against
+    the mirrored oracle at the max-norm bar the full-size modular test uses
+    for fp8 (the derived per-element fp8 bound walks every touched expert in
+    float64), and every token against the modular forward."""
+    _announce("monolithic full deepseek_v3 T=64")
+    moe = _moe()
+    spec = CONFIGS["deepseek_v3"][0]
+    assert spec.T == 64
+    d = make_layer_inputs(spec, device=DEV)
+    w = _weights(moe, d, spec.quant)
+    out, scale = _run(moe, spec, d, w)
+    ref_out, _, _ = moe.moe_forward(d["x"], d["logits"], w, spec.top_k, spec.scoring,
+                                    spec.renormalize, False, spec.activation)
+    torch.cuda.synchronize()
+    a, b = f64_of_bf16(to_numpy_bits(out)), f64_of_bf16(to_numpy_bits(ref_out))
+    assert np.abs(a - b).max() <= 0.06 * np.abs(b).max()
+    hw = {k: to_numpy_bits(d[k]) for k in WKEYS if d.get(k) is not None}
+    tok = np.array([0, 21, 42, spec.T - 1])
+    ref = oracle.forward(to_numpy_bits(d["x"]), d["logits"].cpu().numpy(), hw, spec.top_k,
+                         spec.scoring, spec.renormalize, 16, False, spec.quant, spec.activation,
+                         "mirrored", tokens=tok)
+    check_tolerance(a[tok], None, f64_of_bf16(ref["output"]), "fp8", "monolithic deepseek T=64",
+                    elementwise=False)
+    del d, w
+
+
 def test_monolithic_rejects_what_it_does_not_cover():
     _announce("monolithic limits")
     moe = _moe()
@@ -208,11 +245,15 @@ def test_monolithic_rejects_what_it_does_not_cover():
     lg = torch.zeros((257, spec.E), dtype=torch.float32, device=DEV)
     with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
         moe.moe_forward_monolithic(x, lg, w, spec.top_k)
-    # fp8 weights
-    fspec = _case("decode_split_fp8_mini")
+    # fp8 with per-token activation scales, and fp8 with the weight on the input
+    fspec = _case("fp8_token_mini", T=8)
     fd = {k: v.to(DEV) for k, v in make_layer_inputs(fspec).items()}
-    fw = moe.make_weights(*(fd.get(k) for k in ("w13", "w2", "w13_scale", "w2_scale",
-                                                "shared_w13", "shared_w2", "shared_w13_scale",
-                                                "shared_w2_scale")), quant="fp8")
+    fw = _weights(moe, fd, fspec.quant)
     with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
         moe.moe_forward_monolithic(fd["x"], fd["logits"], fw, fspec.top_k)
+    gspec = _case("gelu_no_mul_fp8_mini", T=8)
+    gd = {k: v.to(DEV) for k, v in make_layer_inputs(gspec).items()}
+    gw = _weights(moe, gd, gspec.quant)
+    with pytest.raises(moe.MoeError, match="UNSUPPORTED"):
+        moe.moe_forward_monolithic(gd["x"], gd["logits"], gw, gspec.top_k, "softmax", False, True,
+                                   gspec.activation)
