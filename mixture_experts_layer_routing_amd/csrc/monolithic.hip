@@ -1,32 +1,37 @@
 // The whole layer in one launch for decode-sized batches: the monolithic
 // mode of "[vLLM] MoE Oracle & Prepare/Finalize" (section on modular vs
 // monolithic kernels: the monolithic mode fuses routing, the experts and
-// finalize into a single kernel), for bf16 weights, T <= 512 and T*top_k <= 512.
+// finalize into a single kernel), for T <= 512 and T*top_k <= 512, bf16
+// weights or fp8 weights (E4M3, 128 x 128 block scales) with G(128)
+// activations.
 //
 // One persistent launch, one 512-thread workgroup per CU the stream may use
-// (all resident at once), four phases with a grid barrier between each two
+// (all resident at once), phases with a grid barrier between each two
 // (grid_sync.h: per-workgroup arrival flags tagged with a per-call epoch,
 // bounded waits):
 //   A  routing: wave t routes token t (route_token, as the routing kernel),
-//      ids and weights to the workspace.
+//      ids and weights to the workspace; fp8: x to E4M3 G(128) as prepare
+//      quantises.
 //   B  first GEMMs: every workgroup sorts the T*top_k routed rows by expert
-//      in LDS (flat-index order within an expert, as align orders them).
-//      Work items, one wave each: (touched expert, 16 z columns) and
-//      (shared expert, 16 z columns).
-//   C  second GEMMs: (touched expert, 16 H columns), (shared expert, 16 H
-//      columns).
-//   D  finalize: workgroup g finalizes tokens g, g+G, ... (weighted sum of
-//      the token's rows, shared row, residual, optional RMSNorm, bf16 or
-//      fp8 G(128) output), as the finalize kernel.
-// A wave computes its 16 output columns for up to 16 rows at a time with
-// 16x16x32 bf16 MFMAs, the weight rows as first operand (lane r of lane
-// group q holds K elements [32s + 8q, +8) of weight row r and of activation
-// row r), both operands loaded from global memory straight into registers,
-// one batch of k-steps ahead: at decode sizes each weight byte is read once
-// and the activation rows (a few KB) come from the L2, so nothing is staged
-// in LDS.  Each output is a plain fp32 sum over K of bf16 products, rounded
-// once to bf16 (z after the activation, y) -- the modular path's arithmetic
-// in another summation order.
+//      in LDS (flat-index order within an expert, as align orders them) and
+//      cuts each expert's rows into 16-row groups.  Work items, one wave
+//      each: (routed group, 16 z columns) and (16 tokens, 16 shared z
+//      columns).  fp8: z stays fp32, and a phase of its own quantises it to
+//      E4M3 G(128) once whole 128-column groups exist.
+//   C  second GEMMs: (routed group, 16 H columns, K slice), (16 tokens, 16
+//      H columns, K slice), fp32 partials.
+//   D  finalize: workgroup g finalizes tokens g, g+G, ... (the slices
+//      summed, the weighted sum of the token's rows, shared row, residual,
+//      optional RMSNorm, bf16 or fp8 G(128) output), as the finalize kernel.
+// A wave computes its 16 output columns for 16 rows at a time with
+// 16x16x32 bf16 MFMAs (fp8: 16x16x128, one per k-tile, promoted with the
+// block scales), the weight rows as first operand, both operands loaded
+// from global memory straight into registers several batches of k-steps
+// ahead: at decode sizes each weight byte is read about once and the
+// activation rows come from the L2, so nothing is staged in LDS.  Each
+// output is a plain fp32 sum over K of the products, rounded once (z after
+// the activation, y) -- the modular path's arithmetic in another summation
+// order.
 #include "moe_device.h"
 #include "launch.h"
 #include "monolithic.h"
