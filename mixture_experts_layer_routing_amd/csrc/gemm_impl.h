@@ -538,6 +538,31 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   const int fm_live = __builtin_amdgcn_readfirstlane(
       valid_rows > row_w ? min(FM, (valid_rows - row_w + MF - 1) / MF) : 0);
 
+  // fp8 tiles of 8 waves below 256 rows (whole partial sets fit beside the
+  // accumulators): k-tile kt's partials and their scale products are
+  // promoted into acc at the start of k-tile kt+1, once its fragment reads
+  // are issued, and after the last k-tile -- in k-tile order, so the sums
+  // are the same.  A wave then goes on to the next barrier while its MFMAs
+  // still run, and the promotion's vector work covers the fragment reads.
+  constexpr bool DEFER = FP8 && SWAP && BM < 256 && gemm_min_waves_per_eu<C>() == 1;
+  acc_t dpart[DEFER ? G : 1][DEFER ? FM : 1][DEFER ? FN : 1];
+  float dsc[DEFER ? G : 1][DEFER ? FM : 1];
+  auto promote_deferred = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    if constexpr (DEFER) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        if (!(FULL || fm < fm_live)) continue;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int v = 0; v < NACC; ++v) acc[g][fm][fn][v] += dpart[g][fm][fn][v] * dsc[g][fm];
+      }
+    }
+  };
+
   // fp8 k-tiles.  A k-tile is one 128-deep scale block: its MFMAs sum into a
   // fresh partial, which is promoted into the fp32 accumulator as
   // acc += partial * s_a[row] * s_w.  The k-tile's activation scales are
@@ -714,6 +739,43 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
         const int r = row_w + fm * MF + (lane & (MF - 1));
         sa_row[fm] = chunked ? sAc[r * 4] : sAb[r];
       }
+    }
+    if constexpr (DEFER) {
+      // both substeps' fragments, then the previous k-tile's promotion, then
+      // this k-tile's MFMAs into the partials it has just read
+      frag_t fa[NSUB][FM], fb[NSUB][G][FN];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          if (FULL || fm < fm_live) fa[s][fm] = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            fb[s][g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+      }
+      if (kt > 0) promote_deferred(full_tag);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          if (FULL || fm < fm_live)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+              for (int fn = 0; fn < FN; ++fn) {
+                if (s == 0) {
+#pragma unroll
+                  for (int v = 0; v < NACC; ++v) dpart[g][fm][fn][v] = 0.f;
+                }
+                dpart[g][fm][fn] = M::mma(fb[s][g][fn], fa[s][fm], dpart[g][fm][fn]);
+              }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int g = 0; g < G; ++g) dsc[g][fm] = sa_row[fm] * swg[g];
+      return;
     }
     acc_t part[G][FM][FN];
 #pragma unroll
@@ -932,8 +994,13 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       nbuf = nbuf + 1 == NSTAGE ? 0 : nbuf + 1;
     }
   };
-  if (fm_live == FM) kloop(std::true_type{});
-  else kloop(std::false_type{});
+  if (fm_live == FM) {
+    kloop(std::true_type{});
+    if (nk > 0) promote_deferred(std::true_type{});
+  } else {
+    kloop(std::false_type{});
+    if (nk > 0) promote_deferred(std::false_type{});
+  }
   __syncthreads();
 
   // ---- epilogue ----
