@@ -97,7 +97,7 @@ def _pmc_means(run_dir, counter, kernel_re=GEMM1_KERNEL_RE):
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no counter_collection.csv under {run_dir}")
-    gemm1, copies = [], []
+    gemm1, copies, names = [], [], set()
     for fn in files:
         for r in csv.DictReader(open(fn)):
             if r["Counter_Name"] != counter:
@@ -105,8 +105,13 @@ def _pmc_means(run_dir, counter, kernel_re=GEMM1_KERNEL_RE):
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
             if re.search(kernel_re, name):
                 gemm1.append(v)
+                names.add(name)
             elif re.search(COPY_KERNEL_RE, name):
                 copies.append((int(r["Dispatch_Id"]), v))
+    if len(names) > 1:
+        # another workload's GEMM (e.g. the decode leg) ran in the same pass
+        raise SystemExit(f"{counter}: {len(names)} different kernels match {kernel_re} in {run_dir}; "
+                         "take the passes with --decode-leg none")
     # the calibration copies are the last three elementwise launches of the run
     copies = [v for _, v in sorted(copies)[-3:]]
     if not gemm1 or len(copies) < 3:

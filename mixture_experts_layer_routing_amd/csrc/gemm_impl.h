@@ -538,12 +538,13 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   const int fm_live = __builtin_amdgcn_readfirstlane(
       valid_rows > row_w ? min(FM, (valid_rows - row_w + MF - 1) / MF) : 0);
 
-  // fp8 tiles of 8 waves below 256 rows (whole partial sets fit beside the
-  // accumulators): k-tile kt's partials and their scale products are
-  // promoted into acc at the start of k-tile kt+1, once its fragment reads
-  // are issued, and after the last k-tile -- in k-tile order, so the sums
-  // are the same.  A wave then goes on to the next barrier while its MFMAs
-  // still run, and the promotion's vector work covers the fragment reads.
+  // fp8 tiles below 256 rows (whole partial sets fit beside the
+  // accumulators; not the tile held to 128 registers, where this spilled):
+  // k-tile kt's partials and their scale products are promoted into acc at
+  // the start of k-tile kt+1, once its fragment reads are issued, and after
+  // the last k-tile -- in k-tile order, so the sums are the same.  A wave
+  // then goes on to the next barrier while its MFMAs still run, and the
+  // promotion's vector work covers the fragment reads.
   constexpr bool DEFER = FP8 && SWAP && BM < 256 && gemm_min_waves_per_eu<C>() == 1;
   acc_t dpart[DEFER ? G : 1][DEFER ? FM : 1][DEFER ? FN : 1];
   float dsc[DEFER ? G : 1][DEFER ? FM : 1];
