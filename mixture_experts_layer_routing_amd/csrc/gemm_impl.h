@@ -49,6 +49,19 @@
 namespace moe {
 
 enum { A_GATHER = 0, A_ROWS = 1, A_DENSE = 2 };
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_from<0, N>(f);
+}
 enum { EPI_Z = 0, EPI_OUT_ROUTED = 1, EPI_OUT_DENSE = 2 };
 
 template <int BM_, int BNZ_, int WAVES_M_, int WAVES_N_, int MF_, bool FP8_, bool GATED_,
@@ -548,6 +561,25 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   constexpr bool DEFER = FP8 && SWAP && BM < 256 && gemm_min_waves_per_eu<C>() == 1;
   acc_t dpart[DEFER ? G : 1][DEFER ? FM : 1][DEFER ? FN : 1];
   float dsc[DEFER ? G : 1][DEFER ? FM : 1];
+  // fp8 tiles of 256 rows (one row fragment's partial set at a time): each
+  // fragment's partial and scale products wait in lpend / lsc until the next
+  // fragment's MFMAs are issued -- the k-tile's last fragment until the next
+  // k-tile's first, or the end -- and are then promoted into row fragment fm
+  // of acc (same products, same order per accumulator).
+  constexpr bool LAG = FP8 && SWAP && BM >= 256;
+  acc_t lpend[LAG ? G : 1][LAG ? FN : 1];
+  float lsc[LAG ? G : 1];
+  auto promote_lag = [&](auto fm_c) {
+    constexpr int fm = decltype(fm_c)::value;
+    if constexpr (LAG) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int v = 0; v < NACC; ++v) acc[g][fm][fn][v] += lpend[g][fn][v] * lsc[g];
+    }
+  };
   auto promote_deferred = [&](auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     if constexpr (DEFER) {
@@ -671,9 +703,10 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
       }
     };
     if constexpr (PER_FRAGMENT) {
-      // 256-row tiles: each row fragment's partial is summed and promoted
-      // before the next one starts, so only one fragment's partial set is
-      // live beside the accumulators (a full partial set would double them).
+      // 256-row tiles: each row fragment's partial is summed, then promoted
+      // once the next fragment's MFMAs are issued (LAG), so at most two
+      // fragments' partials are live beside the accumulators (a full
+      // partial set would double them).
       frag_t fb[NSUB][G][FN];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s)
@@ -682,6 +715,43 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
             fb[s][g][fn] = M::template read<RB>(Bs, g * BNZ + wn * WN + fn * MF + (lane & (MF - 1)), s, lane);
+      if constexpr (LAG) {
+        static_for<FM>([&](auto fm_c) {
+          constexpr int fm = decltype(fm_c)::value;
+          constexpr int pfm = fm == 0 ? FM - 1 : fm - 1;
+          const bool live = FULL || fm < fm_live;
+          acc_t pf[G][FN];
+          if (live) {
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
+              const frag_t fa = M::template read<RB>(As, row_w + fm * MF + (lane & (MF - 1)), s, lane);
+#pragma unroll
+              for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                  if (s == 0) {
+#pragma unroll
+                    for (int v = 0; v < NACC; ++v) pf[g][fn][v] = 0.f;
+                  }
+                  pf[g][fn] = M::mma(fb[s][g][fn], fa, pf[g][fn]);
+                }
+            }
+          }
+          // the pending fragment: fm-1, or the previous k-tile's last
+          if ((fm > 0 || kt > 0) && (FULL || pfm < fm_live)) promote_lag(std::integral_constant<int, pfm>{});
+          if (live) {
+            const int r = row_w + fm * MF + (lane & (MF - 1));
+            const float sa1 = chunked ? sA[((kt >> 2) % NCH) * BM * 4 + r * 4 + (kt & 3)] : sAb[r];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              lsc[g] = sa1 * swg[g];
+#pragma unroll
+              for (int fn = 0; fn < FN; ++fn) lpend[g][fn] = pf[g][fn];
+            }
+          }
+        });
+        return;
+      }
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         if (!(FULL || fm < fm_live)) continue;
@@ -998,9 +1068,11 @@ __global__ __launch_bounds__(64 * C::WAVES_M * C::WAVES_N, gemm_min_waves_per_eu
   if (fm_live == FM) {
     kloop(std::true_type{});
     if (nk > 0) promote_deferred(std::true_type{});
+    if (nk > 0) promote_lag(std::integral_constant<int, FM - 1>{});
   } else {
     kloop(std::false_type{});
     if (nk > 0) promote_deferred(std::false_type{});
+    if (nk > 0 && FM - 1 < fm_live) promote_lag(std::integral_constant<int, FM - 1>{});
   }
   __syncthreads();
 
