@@ -49,6 +49,7 @@
 namespace moe {
 
 enum { A_GATHER = 0, A_ROWS = 1, A_DENSE = 2 };
+enum { EPI_Z = 0, EPI_OUT_ROUTED = 1, EPI_OUT_DENSE = 2 };
 
 // f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
 template <int I, int N, class F>
@@ -62,7 +63,6 @@ template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_from<0, N>(f);
 }
-enum { EPI_Z = 0, EPI_OUT_ROUTED = 1, EPI_OUT_DENSE = 2 };
 
 template <int BM_, int BNZ_, int WAVES_M_, int WAVES_N_, int MF_, bool FP8_, bool GATED_,
           int AMODE_, int EPI_, int NSTAGE_ = 2, int RB_ = 128, bool SPLIT_ = false,
