@@ -178,6 +178,22 @@ int second_gemm_bm(bool fp8, int bm) { return (void)fp8, bm; }
 // fp8 tile stops at 128 rows (two per 256-row block).
 int first_gemm_bm(bool fp8, bool gated, int bm) { return (fp8 && gated) ? std::min(bm, 128) : bm; }
 
+// Output width of the routed first GEMM's tile.  A bf16 gated tile of fewer
+// than 128 rows has 64 z columns by default (gemm_tile_n); it takes 128 (half
+// the tiles, each streaming twice the weight rows against the same gathered
+// rows) while the launch still holds at least two such tiles per CU, by the
+// same block estimate as the K split (n = T*top_k ids, min(E, n) experts
+// touched).  Measured on MI355X: Llama-4 T=128 GEMM-1 0.471 -> 0.457 ms,
+// Mixtral T=32 0.354 -> 0.351 ms; Mixtral T=1 (224 such tiles) 0.083 -> 0.092.
+int first_gemm_bn(bool fp8, bool gated, int bm1, int I, int64_t n, int E) {
+  int bn = moe::gemm_tile_n(moe::GEMM_Z_ROUTED, fp8, gated, bm1, I);
+  if (!fp8 && gated && bn == 64 && I % 128 == 0) {
+    const int64_t touched = std::min<int64_t>(E, n);
+    if ((touched + (n - touched) / bm1) * (I / 128) >= 2 * 256) bn = 128;
+  }
+  return bn;
+}
+
 // The bf16 second GEMM on 256 x 256 tiles runs one workgroup per CU; with
 // fewer than four rounds of tiles (1024) the last round leaves CUs idle, so
 // its K is cut in exactly two (measured on MI355X, Mixtral/Llama-4 shapes:
@@ -229,7 +245,7 @@ SplitPlan split_plan(const Routed& rt, int T, int H, const moe_weights* w, int a
   const int64_t rows = rt.cp.block_cap * bm;
   const int64_t R = gated ? 2 * I : I;
   const int bm1 = first_gemm_bm(fp8, gated, bm);
-  const int bn1 = gemm_tile_n(GEMM_Z_ROUTED, fp8, gated, bm1, I);
+  const int bn1 = first_gemm_bn(fp8, gated, bm1, I, n, E);
   sp.s1 = pick_ksplit(est_blocks(bm1) * (I / bn1), H, ktile, rows, R,
                       static_cast<double>(touched) * R * H * eb);
   const int bm2 = second_gemm_bm(fp8, bm);
@@ -391,7 +407,8 @@ int run_experts(const void* a1q, const float* a1q_scale, const void* shared_in,
   p.K = H;
   p.inter = I;
   const int bm1 = first_gemm_bm(fp8, gated, bm);
-  const int bn1 = gemm_tile_n(GEMM_Z_ROUTED, fp8, gated, bm1, I);
+  const int bn1 = first_gemm_bn(fp8, gated, bm1, I, static_cast<int64_t>(rt.T) * rt.top_k,
+                                w->num_experts);
   p.n_tiles = I / bn1;
   p.sorted = sorted;
   p.block_expert = block_expert;
